@@ -1,0 +1,276 @@
+"""Exact attention forward for AMD MI355X (gfx950): Python binding of libfa.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/fa.h``.  PyTorch supplies device memory
+and the current stream.  The calls mirror the interface described on
+"FlashAttention 常用接口简单介绍" (§3.1-§3.4):
+
+* ``fwd(q, k, v, ...)``            -> (out, softmax_lse)   dense [B, S, H, D]
+* ``fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, ...)``   packed sequences
+* ``fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, ...)``
+* ``combine(out_partial, lse_partial)``
+
+There is no fallback: if libfa.so is missing or a tensor is not on the GPU the
+call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "kvcache_workspace_size",
+           "kvcache_num_splits", "library_path", "load_library", "FaError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa.so")
+_lib = None
+
+FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL, FA_ERR_HIP = range(5)
+_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+
+
+class FaError(RuntimeError):
+    """A libfa call returned FA_ERR_HIP (or an unknown status)."""
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libfa.so (built by ``exact_attention_forward_fa_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m exact_attention_forward_fa_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    OP = ctypes.POINTER(_Opts)
+    lib.fa_fwd.argtypes = [I, P, P, P, P, P, I, I, I, I, I, I, I64P, I64P, I64P, I64P, OP, P]
+    lib.fa_fwd.restype = I
+    lib.fa_fwd_varlen.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I64P, I64P, I64P, I64P, OP, P]
+    lib.fa_fwd_varlen.restype = I
+    lib.fa_kvcache_workspace_size.argtypes = [I, I, I, I, I]
+    lib.fa_kvcache_workspace_size.restype = Z
+    lib.fa_kvcache_num_splits.argtypes = [I, I, I, I]
+    lib.fa_kvcache_num_splits.restype = I
+    lib.fa_fwd_kvcache.argtypes = [I, P, P, P, P, P, I, I, I, I, P, Z, P, P, I, I, I, I, I, OP, P]
+    lib.fa_fwd_kvcache.restype = I
+    lib.fa_combine.argtypes = [P, P, I, I, I, I, I, I64P, I64P, I, P, I64P, P, P]
+    lib.fa_combine.restype = I
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status == FA_OK:
+        return
+    lib = load_library()
+    msg = f"{lib.fa_status_string(status).decode()}: {lib.fa_last_error().decode()}"
+    if status == FA_ERR_INVALID_ARGUMENT:
+        raise ValueError(msg)
+    if status in (FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL):
+        raise NotImplementedError(msg)
+    raise FaError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t, dims):
+    arr = (ctypes.c_int64 * len(dims))(*[t.stride(d) for d in dims])
+    return arr
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, device):
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous float32 CUDA tensor")
+        if alibi_slopes.device != device:
+            raise ValueError("alibi_slopes must be on the same device as q")
+    o = _Opts(0.0 if softmax_scale is None else float(softmax_scale), int(bool(causal)),
+              int(window_size[0]), int(window_size[1]), float(softcap),
+              None if alibi_slopes is None else alibi_slopes.data_ptr())
+    return ctypes.byref(o), o
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+    dev = ts[0].device
+    for t in ts:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+
+
+def _unsupported_kwargs(dropout_p=0.0, return_attn_probs=False):
+    if dropout_p:
+        raise NotImplementedError("dropout_p != 0 is not part of this forward")
+    if return_attn_probs:
+        raise NotImplementedError("return_attn_probs is not supported")
+
+
+def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None,
+        out=None, lse=None, dropout_p=0.0, deterministic=False, return_attn_probs=False):
+    """Dense forward.  q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] fp16/bf16 on the GPU (D stride 1).
+
+    Returns (out [B,Sq,Hq,D], softmax_lse [B,Hq,Sq] float32).  ``deterministic``
+    is accepted and ignored: the forward is deterministic.
+    """
+    _unsupported_kwargs(dropout_p, return_attn_probs)
+    _need_gpu(q, k, v)
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,Sq,Hq,D] and k, v [B,Sk,Hkv,D]")
+    if q.stride(-1) != 1 or k.stride(-1) != 1 or v.stride(-1) != 1:
+        raise ValueError("head_dim must be contiguous")
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("batch / head_dim mismatch")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    _check(lib.fa_fwd(_DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                      B, Sq, Sk, Hq, Hkv, D, _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)),
+                      _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)), ob, _stream(q.device)))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+               causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None, out=None, lse=None,
+               dropout_p=0.0, deterministic=False, return_attn_probs=False):
+    """Packed forward.  q [total_q,Hq,D], k/v [total_k,Hkv,D], cu_seqlens int32 [B+1] on the GPU.
+
+    Returns (out [total_q,Hq,D], softmax_lse [Hq,total_q] float32).
+    """
+    _unsupported_kwargs(dropout_p, return_attn_probs)
+    _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float16 or bfloat16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("expected q [total_q,Hq,D] and k, v [total_k,Hkv,D]")
+    total_q, Hq, D = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    _check(lib.fa_fwd_varlen(_DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                             _ptr(cu_seqlens_q.contiguous()), _ptr(cu_seqlens_k.contiguous()), B,
+                             int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq, Hkv, D,
+                             _strides(q, (0, 1)), _strides(k, (0, 1)), _strides(v, (0, 1)),
+                             _strides(out, (0, 1)), ob, _stream(q.device)))
+    return out, lse
+
+
+def kvcache_workspace_size(B, Sq, Hq, D, num_splits) -> int:
+    return int(load_library().fa_kvcache_workspace_size(B, Sq, Hq, D, num_splits))
+
+
+def kvcache_num_splits(B, Hkv, max_seqlen_k, num_splits=0) -> int:
+    return int(load_library().fa_kvcache_num_splits(B, Hkv, max_seqlen_k, num_splits))
+
+
+def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits=0, softmax_scale=None,
+                causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None, workspace=None,
+                out=None, lse=None, k=None, v=None, cache_leftpad=None, cache_batch_idx=None,
+                return_softmax_lse=True):
+    """Decode against a dense [B,Smax,Hkv,D] cache, or a page pool [P,page,Hkv,D] with block_table int32 [B,maxp].
+
+    Split-KV over ``num_splits`` chunks (0 = library heuristic) followed by the
+    LSE combine.  Returns (out [B,Sq,Hq,D], softmax_lse [B,Hq,Sq]).
+    """
+    if k is not None or v is not None:
+        raise NotImplementedError("appending new k/v to the cache is not supported")
+    if cache_leftpad is not None or cache_batch_idx is not None:
+        raise NotImplementedError("cache_leftpad / cache_batch_idx are not supported")
+    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table)
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share dtype float16 or bfloat16")
+    if cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32")
+    for t in (q, k_cache, v_cache):
+        if not t.is_contiguous():
+            raise ValueError("q, k_cache and v_cache must be contiguous")
+    B, Sq, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be int32 [B, max_pages] with unit last stride")
+        page, nblocks, bts = k_cache.shape[1], k_cache.shape[0], block_table.stride(0)
+        smax_bound = bts * page
+    else:
+        page, nblocks, bts = 0, k_cache.shape[1], 0
+        smax_bound = nblocks
+    lib = load_library()
+    ns = int(lib.fa_kvcache_num_splits(B, Hkv, smax_bound, int(num_splits)))
+    need = int(lib.fa_kvcache_workspace_size(B, Sq, Hq, D, ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    _check(lib.fa_fwd_kvcache(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                              _ptr(block_table), bts, page, nblocks, ns, _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                              B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
+    return (out, lse) if return_softmax_lse else out
+
+
+def combine(out_partial, lse_partial, out_dtype=None, out=None, lse=None):
+    """Merge split partials: out_partial [B,S,H,D,n] and lse_partial [B,S,H,n] float32 (any strides).
+
+    Returns (out [B,S,H,D] in out_dtype (default float16), lse [B,S,H] float32).
+    """
+    _need_gpu(out_partial, lse_partial)
+    if out_partial.dtype != torch.float32 or lse_partial.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    B, S, H, D, n = out_partial.shape
+    if tuple(lse_partial.shape) != (B, S, H, n):
+        raise ValueError("lse_partial must be [B,S,H,num_splits]")
+    out_dtype = out_dtype or torch.float16
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=out_dtype, device=out_partial.device)
+    if lse is None:
+        lse = torch.empty((B, S, H), dtype=torch.float32, device=out_partial.device)
+    lib = load_library()
+    _check(lib.fa_combine(_ptr(out_partial), _ptr(lse_partial), B, S, H, D, n,
+                          _strides(out_partial, (0, 1, 2, 3, 4)), _strides(lse_partial, (0, 1, 2, 3)),
+                          _DTYPES[out.dtype], _ptr(out), _strides(out, (0, 1, 2)), _ptr(lse),
+                          _stream(out_partial.device)))
+    return out, lse

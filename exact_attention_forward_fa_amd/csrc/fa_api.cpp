@@ -1,0 +1,309 @@
+// Host side of the C ABI declared in include/fa.h: argument validation,
+// defaults, workspace layout and kernel launches on the caller's stream.
+// Validation never touches the HIP runtime, so every error path can be
+// exercised on a machine without a GPU.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fa_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa_status ok() {
+  g_last_error.clear();
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status check_opts(const fa_attn_opts* o, int D, float* scale_out) {
+  float scale = 0.f;
+  if (o) {
+    if (!std::isfinite(o->softmax_scale)) return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+    if (o->window_left < -1 || o->window_right < -1)
+      return fail(FA_ERR_INVALID_ARGUMENT, "window (%d, %d): each side must be >= -1", o->window_left, o->window_right);
+    if (!std::isfinite(o->softcap) || o->softcap < 0.f)
+      return fail(FA_ERR_INVALID_ARGUMENT, "softcap must be finite and >= 0");
+    scale = o->softmax_scale;
+  }
+  *scale_out = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  return FA_OK;
+}
+
+fa_status check_common(int dtype, int Hq, int Hkv, int D) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "Hkv=%d must divide Hq=%d", Hkv, Hq);
+  if (D <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "head_dim must be positive (D=%d)", D);
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", D);
+  return FA_OK;
+}
+
+fa_status check_strides(const char* name, const int64_t* s, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s stride %d is negative", name, i);
+    if (s[i] % 8 != 0) return fail(FA_ERR_UNSUPPORTED, "%s stride %d (%lld elements) is not a multiple of 8", name, i, (long long)s[i]);
+  }
+  return FA_OK;
+}
+
+void fill_opts(fa::PrefillParams& p, const fa_attn_opts* o, float scale) {
+  p.scale = scale;
+  p.softcap = o ? o->softcap : 0.f;
+  p.alibi = o ? o->alibi_slopes : nullptr;
+  p.causal = o ? (o->causal != 0) : 0;
+  p.wl = o ? o->window_left : -1;
+  p.wr = o ? o->window_right : -1;
+}
+
+fa_status launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "FA_ERR_WORKSPACE_TOO_SMALL";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                 const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                 const int64_t* o_stride, const fa_attn_opts* opts, void* stream) {
+  fa_status st = check_common(dtype, Hq, Hkv, D);
+  if (st) return st;
+  if (B < 0 || Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Sk=%d)", B, Sq, Sk);
+  float scale;
+  if ((st = check_opts(opts, D, &scale))) return st;
+  if (B == 0 || Sq == 0) return ok();
+  if (!q || !k || !v || !out || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FA_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
+  const int64_t qd[3] = {(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
+  const int64_t kd[3] = {(int64_t)Sk * Hkv * D, (int64_t)Hkv * D, D};
+  const int64_t* qs = q_stride ? q_stride : qd;
+  const int64_t* ks = k_stride ? k_stride : kd;
+  const int64_t* vs = v_stride ? v_stride : kd;
+  const int64_t* os = o_stride ? o_stride : qd;
+  if ((st = check_strides("q", qs, 3)) || (st = check_strides("k", ks, 3)) || (st = check_strides("v", vs, 3)) ||
+      (st = check_strides("out", os, 3)))
+    return st;
+  const int64_t nqt = (Sq + fa::kPrefillBlockM - 1) / fa::kPrefillBlockM;
+  if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+
+  fa::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.q_sb = qs[0]; p.q_ss = qs[1]; p.q_sh = qs[2];
+  p.k_sb = ks[0]; p.k_ss = ks[1]; p.k_sh = ks[2];
+  p.v_sb = vs[0]; p.v_ss = vs[1]; p.v_sh = vs[2];
+  p.o_sb = os[0]; p.o_ss = os[1]; p.o_sh = os[2];
+  p.lse_sb = (int64_t)Hq * Sq; p.lse_sh = Sq;
+  p.cu_seqlens_q = nullptr; p.cu_seqlens_k = nullptr;
+  p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  fill_opts(p, opts, scale);
+  p.n_qtiles = (int)nqt;
+  p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
+  return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "prefill launch");
+}
+
+fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                        int Hq, int Hkv, int D,
+                        const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                        const int64_t* o_stride, const fa_attn_opts* opts, void* stream) {
+  fa_status st = check_common(dtype, Hq, Hkv, D);
+  if (st) return st;
+  if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  float scale;
+  if ((st = check_opts(opts, D, &scale))) return st;
+  if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ok();
+  if (!q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(FA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FA_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
+  const int64_t qd[2] = {(int64_t)Hq * D, D};
+  const int64_t kd[2] = {(int64_t)Hkv * D, D};
+  const int64_t* qs = q_stride ? q_stride : qd;
+  const int64_t* ks = k_stride ? k_stride : kd;
+  const int64_t* vs = v_stride ? v_stride : kd;
+  const int64_t* os = o_stride ? o_stride : qd;
+  if ((st = check_strides("q", qs, 2)) || (st = check_strides("k", ks, 2)) || (st = check_strides("v", vs, 2)) ||
+      (st = check_strides("out", os, 2)))
+    return st;
+  const int64_t nqt = (max_seqlen_q + fa::kPrefillBlockM - 1) / fa::kPrefillBlockM;
+  if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+
+  fa::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.q_sb = 0; p.q_ss = qs[0]; p.q_sh = qs[1];
+  p.k_sb = 0; p.k_ss = ks[0]; p.k_sh = ks[1];
+  p.v_sb = 0; p.v_ss = vs[0]; p.v_sh = vs[1];
+  p.o_sb = 0; p.o_ss = os[0]; p.o_sh = os[1];
+  p.lse_sb = 0; p.lse_sh = total_q;
+  p.cu_seqlens_q = cu_seqlens_q; p.cu_seqlens_k = cu_seqlens_k;
+  p.B = B; p.Sq = max_seqlen_q; p.Sk = max_seqlen_k; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  fill_opts(p, opts, scale);
+  p.n_qtiles = (int)nqt;
+  p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
+  return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "varlen prefill launch");
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t fa_kvcache_workspace_size(int B, int Sq, int Hq, int D, int num_splits) {
+  if (B <= 0 || Sq <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * Sq * Hq * num_splits;
+  return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  const int64_t groups = (int64_t)(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
+  int64_t n = (1024 + groups - 1) / groups;              // ~4 workgroups per CU
+  const int64_t by_len = (int64_t)(max_seqlen_k > 0 ? max_seqlen_k : 1) / 64;
+  if (n > by_len) n = by_len;
+  if (n < 1) n = 1;
+  if (n > 64) n = 64;
+  return (int)n;
+}
+
+fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
+                         const int* cache_seqlens, const int* block_table, int block_table_stride,
+                         int page_size, int num_blocks_or_smax, int num_splits,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse,
+                         int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream) {
+  fa_status st = check_common(dtype, Hq, Hkv, D);
+  if (st) return st;
+  if (B < 0 || Sq < 0 || num_blocks_or_smax < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (num_splits > 64) return fail(FA_ERR_UNSUPPORTED, "num_splits %d > 64", num_splits);
+  if (block_table && (page_size <= 0 || block_table_stride <= 0))
+    return fail(FA_ERR_INVALID_ARGUMENT, "paged cache needs page_size > 0 and block_table_stride > 0");
+  float scale;
+  if ((st = check_opts(opts, D, &scale))) return st;
+  if ((Hq / Hkv) * (int64_t)Sq > 16)
+    return fail(FA_ERR_UNSUPPORTED, "(Hq/Hkv)*Sq = %lld query rows per kv head; at most 16 are built",
+                (long long)(Hq / Hkv) * Sq);
+  if (B == 0 || Sq == 0) return ok();
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !out || !lse)
+    return fail(FA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FA_ERR_UNSUPPORTED, "q/k_cache/v_cache must be 16-byte aligned");
+  const int smax_bound = block_table ? block_table_stride * page_size : num_blocks_or_smax;
+  const int ns = fa_kvcache_num_splits(B, Hkv, smax_bound, num_splits);
+  const size_t need = fa_kvcache_workspace_size(B, Sq, Hq, D, ns);
+  if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "null workspace");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+
+  const size_t rows = (size_t)B * Sq * Hq * ns;
+  float* op = static_cast<float*>(workspace);
+  float* lp = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * D * sizeof(float)));
+
+  fa::DecodeParams d{};
+  d.q = q; d.k = k_cache; d.v = v_cache;
+  d.cache_seqlens = cache_seqlens;
+  d.block_table = block_table;
+  d.bt_stride = block_table_stride;
+  d.page_size = block_table ? page_size : num_blocks_or_smax;
+  d.log2_page = -1;
+  if (block_table && (page_size & (page_size - 1)) == 0) {
+    int lg = 0;
+    while ((1 << lg) < page_size) ++lg;
+    d.log2_page = lg;
+  }
+  d.out_partial = op; d.lse_partial = lp;
+  d.B = B; d.Sq = Sq; d.Hq = Hq; d.Hkv = Hkv; d.group = Hq / Hkv;
+  d.num_splits = ns;
+  d.scale = scale;
+  d.softcap = opts ? opts->softcap : 0.f;
+  d.alibi = opts ? opts->alibi_slopes : nullptr;
+  d.causal = opts ? (opts->causal != 0) : 0;
+  d.wl = opts ? opts->window_left : -1;
+  d.wr = opts ? opts->window_right : -1;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = fa::launch_decode((fa::Dtype)dtype, D, d, s);
+  if (e != hipSuccess) return launch_status(e, "decode launch");
+
+  fa::CombineParams c{};
+  c.out_partial = op; c.lse_partial = lp;
+  c.op_sn = D; c.op_sd = 1; c.op_sh = (int64_t)ns * D; c.op_ss = c.op_sh * Hq; c.op_sb = c.op_ss * Sq;
+  c.lp_sn = 1; c.lp_sh = ns; c.lp_ss = (int64_t)ns * Hq; c.lp_sb = c.lp_ss * Sq;
+  c.out = out;
+  c.o_sh = D; c.o_ss = (int64_t)Hq * D; c.o_sb = c.o_ss * Sq;
+  c.lse = lse;
+  c.l_sh = Sq; c.l_ss = 1; c.l_sb = (int64_t)Hq * Sq;
+  c.B = B; c.S = Sq; c.H = Hq; c.D = D; c.num_splits = ns;
+  return launch_status(fa::launch_combine((fa::Dtype)dtype, c, s), "combine launch");
+}
+
+fa_status fa_combine(const float* out_partial, const float* lse_partial, int B, int S, int H, int D,
+                     int num_splits, const int64_t* op_stride, const int64_t* lp_stride,
+                     fa_dtype out_dtype, void* out, const int64_t* o_stride, float* lse, void* stream) {
+  if (out_dtype != FA_F16 && out_dtype != FA_BF16) return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype %d", out_dtype);
+  if (B < 0 || S < 0 || H < 0 || D <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "bad size");
+  if (num_splits < 1) return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be >= 1");
+  if (num_splits > 64) return fail(FA_ERR_UNSUPPORTED, "num_splits %d > 64", num_splits);
+  if ((int64_t)B * S * H == 0) return ok();
+  if (!out_partial || !lse_partial || !out) return fail(FA_ERR_INVALID_ARGUMENT, "null pointer");
+  const int64_t opd[5] = {(int64_t)S * H * D * num_splits, (int64_t)H * D * num_splits, (int64_t)D * num_splits,
+                          num_splits, 1};
+  const int64_t lpd[4] = {(int64_t)S * H * num_splits, (int64_t)H * num_splits, num_splits, 1};
+  const int64_t od[3] = {(int64_t)S * H * D, (int64_t)H * D, D};
+  const int64_t* os = op_stride ? op_stride : opd;
+  const int64_t* ls = lp_stride ? lp_stride : lpd;
+  const int64_t* oo = o_stride ? o_stride : od;
+  for (int i = 0; i < 5; ++i)
+    if (os[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative out_partial stride");
+  for (int i = 0; i < 4; ++i)
+    if (ls[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative lse_partial stride");
+  for (int i = 0; i < 3; ++i)
+    if (oo[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative out stride");
+  if (((int64_t)B * S * H + 3) / 4 > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  fa::CombineParams c{};
+  c.out_partial = out_partial; c.lse_partial = lse_partial;
+  c.op_sb = os[0]; c.op_ss = os[1]; c.op_sh = os[2]; c.op_sd = os[3]; c.op_sn = os[4];
+  c.lp_sb = ls[0]; c.lp_ss = ls[1]; c.lp_sh = ls[2]; c.lp_sn = ls[3];
+  c.out = out; c.o_sb = oo[0]; c.o_ss = oo[1]; c.o_sh = oo[2];
+  c.lse = lse; c.l_sb = (int64_t)S * H; c.l_ss = H; c.l_sh = 1;
+  c.B = B; c.S = S; c.H = H; c.D = D; c.num_splits = num_splits;
+  return launch_status(fa::launch_combine((fa::Dtype)out_dtype, c, (hipStream_t)stream), "combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Device helpers for the gfx950 (CDNA4) attention kernels: element types,
+// MFMA wrappers, conversions, exp2 and cross-lane operations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Element traits: storage type, 8-wide MFMA operand vector, packed pair.
+struct F16 {
+  typedef _Float16 T;
+  typedef f16x8 V8;
+  typedef f16x2 V2;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // round-to-nearest-even pack of two floats (v_cvt_pk_f16_f32)
+  static __device__ __forceinline__ V2 pack(float a, float b) {
+    V2 r; r[0] = (T)a; r[1] = (T)b; return r;
+  }
+  // fp32 accumulate of the pair's sum: a.x*1 + a.y*1 + c (v_dot2c_f32_f16)
+  static __device__ __forceinline__ float sum2(V2 a, float c) {
+    const V2 one = {(T)1.0f, (T)1.0f};
+    return __builtin_amdgcn_fdot2(a, one, c, false);
+  }
+  static __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+  static __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+};
+
+struct BF16 {
+  typedef __bf16 T;
+  typedef bf16x8 V8;
+  typedef bf16x2 V2;
+  static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ V2 pack(float a, float b) {
+    V2 r; r[0] = (T)a; r[1] = (T)b; return r;
+  }
+  static __device__ __forceinline__ float sum2(V2 a, float c) {
+    const V2 one = {(T)1.0f, (T)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(a, one, c, false);
+  }
+  static __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+  static __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of x held by the lane in the other 32-lane half (lane l <-> l ^ 32).
+__device__ __forceinline__ float other_half(float x) {
+  u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes 0..31 receive the upper half's value in r[1]; lanes 32..63 in r[0]
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// max / sum of x over the pair of lanes {l, l ^ 32}
+__device__ __forceinline__ float max_halves(float x) {
+  u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte chunk addressed by lane
+// 4*j + i/4, for j = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p));
+}
+
+}  // namespace fa

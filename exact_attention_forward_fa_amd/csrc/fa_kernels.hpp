@@ -1,0 +1,78 @@
+// Parameter blocks and launcher entry points shared by the C-ABI host layer
+// (fa_api.cpp) and the kernel translation units.  Everything here is plain
+// data: device pointers, sizes and element strides.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum Dtype { kF16 = 0, kBF16 = 1 };
+
+// Prefill (dense or packed variable-length) forward.
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  // element strides: batch, sequence, head (head_dim stride is 1)
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t lse_sb, lse_sh;      // lse element (b, h, i) at b*lse_sb + h*lse_sh + row_base + i
+  const int* cu_seqlens_q;     // varlen: [B+1] prefix sums (nullptr for dense)
+  const int* cu_seqlens_k;
+  int B, Sq, Sk;               // dense sizes; for varlen Sq/Sk hold max_seqlen_q/k
+  int Hq, Hkv, group;          // group = Hq / Hkv
+  float scale;                 // softmax scale
+  float softcap;               // 0 = off
+  const float* alibi;          // [Hq] slopes or nullptr
+  int causal;
+  int wl, wr;                  // window (left, right), -1 = unbounded
+  int n_qtiles;                // ceil(Sq / BLOCK_M)
+  int remap_xcd;               // 1 when the grid size is a multiple of 8
+};
+
+// Split-KV decode over a dense or paged cache: partial results per split.
+struct DecodeParams {
+  const void* q;               // [B, Sq, Hq, D]
+  const void* k;               // dense [B, Smax, Hkv, D] or pool [P, page, Hkv, D]
+  const void* v;
+  const int* cache_seqlens;    // [B]
+  const int* block_table;      // [B, bt_stride] or nullptr (dense)
+  int bt_stride;
+  int page_size;               // paged: tokens per page; dense: Smax
+  int log2_page;               // log2(page_size) when page_size is a power of two, else -1
+  float* out_partial;          // [B, Sq, Hq, num_splits, D] fp32
+  float* lse_partial;          // [B, Sq, Hq, num_splits] fp32
+  int B, Sq, Hq, Hkv, group;
+  int num_splits;
+  float scale;
+  float softcap;
+  const float* alibi;
+  int causal;
+  int wl, wr;
+};
+
+// LSE-weighted merge of split partials.
+struct CombineParams {
+  const float* out_partial;
+  const float* lse_partial;
+  int64_t op_sb, op_ss, op_sh, op_sd, op_sn;   // element strides of out_partial (b, s, h, d, split)
+  int64_t lp_sb, lp_ss, lp_sh, lp_sn;          // element strides of lse_partial (b, s, h, split)
+  void* out;
+  int64_t o_sb, o_ss, o_sh;                    // out element strides (d stride 1)
+  float* lse;                                  // optional
+  int64_t l_sb, l_ss, l_sh;                    // lse element strides
+  int B, S, H, D, num_splits;
+};
+
+hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s);
+hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s);
+hipError_t launch_combine(Dtype dt, const CombineParams& p, hipStream_t s);
+
+constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup
+
+}  // namespace fa

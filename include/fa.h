@@ -1,0 +1,150 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact attention forward library, libfa.so.
+ *
+ * The library computes exact attention, out = softmax(scale * Q Kᵀ) V, tile by
+ * tile with an online softmax so that the Sq x Sk score matrix never reaches
+ * HBM, and returns the per-row log-sum-exp next to the output.  The calls and
+ * their options follow the Python interface described on
+ * "FlashAttention 常用接口简单介绍" (xllm-io.github.io): §3.1 flash_attn_func,
+ * §3.2 flash_attn_varlen_func, §3.3 flash_attn_with_kvcache, §3.4
+ * flash_attn_combine; the option semantics come from the Flash-Attention
+ * v2.0-v2.7 update notes (framerc.cn): bottom-right causal alignment, v2.2
+ * split-KV, v2.3 sliding window, v2.4 ALiBi, v2.5 paged KV cache, v2.6 softcap.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains device memory, and inputs are read-only.
+ *  - Element type: fa_dtype (fp16 or bf16) for q/k/v/out; float32 for lse,
+ *    ALiBi slopes and the decode workspace; int32 for cu_seqlens,
+ *    cache_seqlens and block_table.
+ *  - Head dimension D must be 64 or 128; the head-dim stride is 1 and row
+ *    starts must be 16-byte aligned (strides multiples of 8 elements, base
+ *    pointers 16-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns without synchronising; results
+ *    are valid once the stream has reached that point.
+ *  - Every element of out and lse is written, including rows that have no
+ *    allowed key: out = 0 and lse = -inf there.
+ *  - Errors: host-side checks run before anything is enqueued; on any error
+ *    nothing is launched and a status other than FA_OK is returned, with a
+ *    thread-local message available from fa_last_error().  B == 0 or an empty
+ *    query side is a valid no-op.  Device-side contents (monotonic cu_seqlens,
+ *    in-range block_table entries, cache_seqlens within the cache) are the
+ *    caller's contract and are not checked.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, Hq % Hkv != 0, window < -1, ... */
+  FA_ERR_UNSUPPORTED = 2,        /* valid but not built: D not in {64,128}, misalignment, ... */
+  FA_ERR_WORKSPACE_TOO_SMALL = 3,/* decode workspace below fa_kvcache_workspace_size() */
+  FA_ERR_HIP = 4                 /* a HIP launch error; fa_last_error() carries its text */
+} fa_status;
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Attention options ("FlashAttention 常用接口简单介绍", §3.1 keyword arguments). */
+typedef struct {
+  float softmax_scale;          /* <= 0 selects the default 1/sqrt(D)                           */
+  int causal;                   /* nonzero: key j allowed for query i iff j <= i + Sk - Sq       */
+  int window_left;              /* local window: keys in [i' - left, i' + right], i' = i + Sk - Sq; */
+  int window_right;             /*   -1 = unbounded on that side; both -1 = global attention    */
+  float softcap;                /* > 0: score s becomes softcap * tanh(s / softcap); 0 = off    */
+  const float* alibi_slopes;    /* device float32 [Hq]: score -= slope[h] * |i' - j|; NULL = off */
+} fa_attn_opts;
+
+/*
+ * Dense forward ("FlashAttention 常用接口简单介绍", §3.1 flash_attn_func).
+ *   q   [B, Sq, Hq, D], k/v [B, Sk, Hkv, D], out [B, Sq, Hq, D] (dtype),
+ *   lse [B, Hq, Sq] float32, contiguous.
+ *   *_stride: element strides of the (batch, sequence, head) dimensions; NULL
+ *   means the contiguous [B, S, H, D] layout.
+ *   Hkv must divide Hq (GQA/MQA: query head h reads kv head h / (Hq/Hkv)).
+ *   opts may be NULL (defaults: scale 1/sqrt(D), no mask, no softcap, no ALiBi).
+ */
+fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                 const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                 const int64_t* o_stride, const fa_attn_opts* opts, void* stream);
+
+/*
+ * Packed variable-length forward ("FlashAttention 常用接口简单介绍", §3.2).
+ *   q [total_q, Hq, D], k/v [total_k, Hkv, D], out [total_q, Hq, D],
+ *   lse [Hq, total_q] float32.  cu_seqlens_q/k: device int32 [B+1] prefix sums;
+ *   sequence b owns rows [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]) and
+ *   is masked/aligned on its own lengths.  max_seqlen_q/k bound every
+ *   sequence's length (the grid is sized from max_seqlen_q).
+ *   *_stride: element strides of the (token, head) dimensions; NULL = contiguous.
+ */
+fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B,
+                        int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                        int Hq, int Hkv, int D,
+                        const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                        const int64_t* o_stride, const fa_attn_opts* opts, void* stream);
+
+/* Bytes of float32 workspace fa_fwd_kvcache needs: B*Sq*Hq*num_splits*(D+1)*4,
+ * the out partials padded to 256 bytes, then the lse partials. num_splits as
+ * passed to fa_fwd_kvcache after resolving 0 (see fa_kvcache_num_splits). */
+size_t fa_kvcache_workspace_size(int B, int Sq, int Hq, int D, int num_splits);
+
+/* The split count fa_fwd_kvcache uses when passed num_splits = 0, for a cache
+ * whose sequences hold at most max_seqlen_k tokens: enough workgroups to fill
+ * the GPU, at least 64 tokens per split, at most 64 splits. */
+int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits);
+
+/*
+ * Decode against a KV cache ("FlashAttention 常用接口简单介绍", §3.3), split along
+ * the cache sequence into num_splits chunks (update notes, v2.2) and merged by
+ * a separate LSE-weighted combine kernel (§3.4).
+ *   q [B, Sq, Hq, D] contiguous, out [B, Sq, Hq, D] contiguous, lse [B, Hq, Sq].
+ *   block_table == NULL: k_cache/v_cache are dense [B, num_blocks_or_smax, Hkv, D].
+ *   block_table != NULL: k_cache/v_cache are page pools [num_blocks_or_smax,
+ *     page_size, Hkv, D] and block_table is int32 [B, block_table_stride]; token
+ *     t of sequence b lives in page block_table[b, t / page_size], row
+ *     t % page_size (update notes, v2.5).
+ *   cache_seqlens: device int32 [B], tokens attended per sequence; the Sq
+ *     queries are bottom-right aligned against them.
+ *   num_splits: 1..64, or 0 for fa_kvcache_num_splits(); (Hq/Hkv)*Sq <= 16.
+ *   workspace: device memory of at least fa_kvcache_workspace_size() bytes,
+ *     256-byte aligned; it holds the per-split partials between the two kernels.
+ */
+fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
+                         const int* cache_seqlens, const int* block_table, int block_table_stride,
+                         int page_size, int num_blocks_or_smax, int num_splits,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse,
+                         int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream);
+
+/*
+ * Merge split partial results by their log-sum-exp ("FlashAttention 常用接口简单介绍",
+ * §3.4 flash_attn_combine).  out_partial [B, S, H, D, num_splits] and
+ * lse_partial [B, S, H, num_splits] float32; op_stride (5 entries: b, s, h, d,
+ * split) and lp_stride (4 entries: b, s, h, split) give element strides, NULL =
+ * contiguous in that order.  out [B, S, H, D] of out_dtype (o_stride: b, s, h;
+ * NULL = contiguous); lse [B, S, H] float32 contiguous, may be NULL.
+ * 1 <= num_splits <= 64.  out = Σ_s exp(lse_s - lse) out_s, lse = log Σ_s exp(lse_s).
+ */
+fa_status fa_combine(const float* out_partial, const float* lse_partial, int B, int S, int H, int D,
+                     int num_splits, const int64_t* op_stride, const int64_t* lp_stride,
+                     fa_dtype out_dtype, void* out, const int64_t* o_stride, float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(fa_status status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/fa.h declares, and rejects bad arguments with the documented status
+before anything is launched (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_forward_fa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_combine", "fa_kvcache_workspace_size",
+            "fa_kvcache_num_splits", "fa_status_string", "fa_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libfa.so"
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["FA_OK", "FA_ERR_INVALID_ARGUMENT", "FA_ERR_UNSUPPORTED",
+                                 "FA_ERR_WORKSPACE_TOO_SMALL", "FA_ERR_HIP"]):
+        assert lib.fa_status_string(code).decode() == name
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced: validation fails first
+
+
+def _opts(**kw):
+    o = fa._Opts(kw.get("scale", 0.0), kw.get("causal", 0), kw.get("wl", -1), kw.get("wr", -1),
+                 kw.get("softcap", 0.0), None)
+    return ctypes.byref(o), o
+
+
+def fwd(lib, dtype=0, B=1, Sq=8, Sk=8, Hq=2, Hkv=2, D=64, ptrs=None, strides=None, **o):
+    ob, keep = _opts(**o)
+    p = ptrs or [FAKE] * 5
+    s = strides or [None] * 4
+    return lib.fa_fwd(dtype, *p, B, Sq, Sk, Hq, Hkv, D, *s, ob, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 1),
+    (dict(Hq=3, Hkv=2), 1),
+    (dict(Hkv=0), 1),
+    (dict(D=0), 1),
+    (dict(D=96), 2),
+    (dict(D=256), 2),
+    (dict(B=-1), 1),
+    (dict(Sk=-3), 1),
+    (dict(wl=-2), 1),
+    (dict(wr=-5), 1),
+    (dict(softcap=-1.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(ptrs=[FAKE, None, FAKE, FAKE, FAKE]), 1),
+    (dict(ptrs=[ctypes.c_void_p((1 << 20) + 2)] + [FAKE] * 4), 2),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_fwd_stride_checks(lib):
+    bad = (ctypes.c_int64 * 3)(1000, 12, 64)          # 12 not a multiple of 8
+    assert fwd(lib, strides=[bad, None, None, None]) == 2
+    neg = (ctypes.c_int64 * 3)(-8, 128, 64)
+    assert fwd(lib, strides=[None, neg, None, None]) == 1
+
+
+def test_noop_sizes_return_ok(lib):
+    assert fwd(lib, B=0, ptrs=[None] * 5) == 0
+    assert fwd(lib, Sq=0, ptrs=[None] * 5) == 0
+
+
+def test_varlen_rejects(lib):
+    ob, keep = _opts()
+    f = lambda **k: lib.fa_fwd_varlen(k.get("dtype", 0), FAKE, FAKE, FAKE, FAKE, FAKE, k.get("cu", FAKE), FAKE,
+                                      k.get("B", 2), 16, 16, 32, 32, k.get("Hq", 4), 2, k.get("D", 64),
+                                      None, None, None, None, ob, None)
+    assert f(cu=None) == 1
+    assert f(Hq=3) == 1
+    assert f(D=80) == 2
+    assert f(B=-1) == 1
+
+
+def test_kvcache_workspace_and_rejects(lib):
+    assert lib.fa_kvcache_workspace_size(64, 1, 32, 128, 16) == 64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
+    assert lib.fa_kvcache_workspace_size(1, 1, 1, 64, 3) == 768 + 256
+    assert lib.fa_kvcache_num_splits(64, 8, 16384, 16) == 16
+    assert 1 <= lib.fa_kvcache_num_splits(64, 8, 16384, 0) <= 64
+    assert lib.fa_kvcache_num_splits(1, 1, 100, 0) == 1
+    ob, keep = _opts()
+
+    def kv(ws=FAKE, wsb=1 << 30, ns=16, Hq=32, Hkv=8, Sq=1, bt=FAKE, page=256, bts=64):
+        return lib.fa_fwd_kvcache(1, FAKE, FAKE, FAKE, FAKE, bt, bts, page, 100, ns, ws, wsb, FAKE, FAKE,
+                                  4, Sq, Hq, Hkv, 128, ob, None)
+    assert kv(wsb=100) == 3
+    assert kv(ws=None) == 1
+    assert kv(ws=ctypes.c_void_p((1 << 20) + 16)) == 2
+    assert kv(ns=65) == 2
+    assert kv(ns=-1) == 1
+    assert kv(Hq=32, Hkv=1) == 2              # 32 query rows per kv head > 16
+    assert kv(Sq=5) == 2                      # 4 * 5 = 20 rows > 16
+    assert kv(page=0) == 1
+    assert kv(bts=0) == 1
+
+
+def test_combine_rejects(lib):
+    f = lambda **k: lib.fa_combine(FAKE, FAKE, 1, 1, 1, k.get("D", 64), k.get("ns", 4), None, None,
+                                   k.get("dt", 0), k.get("out", FAKE), None, None, None)
+    assert f(ns=0) == 1
+    assert f(ns=65) == 2
+    assert f(dt=5) == 1
+    assert f(out=None) == 1
+    assert f(D=0) == 1
+
+
+def test_python_layer_rejects_unsupported_kwargs():
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        fa.fwd(q, q, q, dropout_p=0.1)
+    with pytest.raises(NotImplementedError):
+        fa.fwd(q, q, q, return_attn_probs=True)
+    with pytest.raises(NotImplementedError):
+        fa.fwd_kvcache(q, q, q, torch.zeros(1, dtype=torch.int32), k=q)
+    with pytest.raises(ValueError):          # CPU tensors: no fallback path exists
+        fa.fwd(q, q, q)
