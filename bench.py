@@ -1,0 +1,240 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one pass of the whole hot path on resident inputs:
+  * prefill: causal attention, B=4, Sq=Sk=4096, Hq=Hkv=32, D=64, fp16
+    (one fa_fwd launch of the MFMA prefill kernel);
+  * decode: paged split-KV decode, B=64, Sq=1, Hq=32, Hkv=8, D=128, bf16,
+    per-sequence cache length uniform in [1024, 16384], 256-token pages with a
+    permuted block table, 16 splits + the LSE combine (one fa_fwd_kvcache call).
+
+Prints ONE JSON line.  value = prefill TFLOP/s over algorithmic FLOPs
+(4·D per allowed (query, key) pair, masked area excluded) divided by the
+prefill kernel's mean duration from HIP events on the launch stream; the
+decode figure (GB/s of algorithmic K/V/q/out/block-table bytes over the
+decode + combine time) rides along in "decode".  "cpu_baseline" times the
+float64 CPU oracle on a bounded sample of the prefill workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def causal_pairs(Sq: int, Sk: int) -> int:
+    """Allowed (query, key) pairs of one head under bottom-right causal masking."""
+    shift = Sk - Sq
+    # row i sees keys 0..min(Sk-1, i+shift): count = clamp(i + shift + 1, 0, Sk)
+    total = 0
+    lo = max(0, -shift)                      # first row with at least one key
+    full_from = max(lo, Sk - 1 - shift)      # rows from here on see all Sk keys
+    if full_from > lo:
+        a, b = lo + shift + 1, full_from - 1 + shift + 1
+        total += (a + b) * (full_from - lo) // 2
+    total += max(0, Sq - full_from) * Sk
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "fa_device.hpp", "fa_kernels.hpp"):
+        with open(os.path.join(ROOT, "exact_attention_forward_fa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- CPU oracle leg
+
+def _oracle_head(args):
+    q, k, v = args
+    from oracle import ref
+    t = time.perf_counter()
+    ref.attention(q[None, :, None], k[None, :, None], v[None, :, None], causal=True)
+    return time.perf_counter() - t
+
+
+def cpu_baseline(case, n_heads: int, workers: int):
+    """Time the float64 oracle on n_heads (batch, head) pairs of the prefill workload."""
+    import numpy as np
+    q, k, v = case["q"], case["k"], case["v"]
+    B, S, H, D = q.shape
+    pairs = [(i // H, i % H) for i in range(min(n_heads, B * H))]
+    jobs = [(q[b, :, h].float().numpy().astype(np.float64), k[b, :, h].float().numpy().astype(np.float64),
+             v[b, :, h].float().numpy().astype(np.float64)) for b, h in pairs]
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_head, jobs, chunksize=1)
+    wall = time.perf_counter() - t0
+    flops = 4 * D * causal_pairs(S, S) * len(pairs)
+    return dict(value=flops / wall / 1e12, unit="TFLOP/s", cores=workers, kind="oracle",
+                sample=f"float64 oracle, causal, {len(pairs)} of {B * H} (batch, head) pairs of the "
+                       f"B{B} S{S} H{H} D{D} prefill, all {S} rows each, {workers} single-threaded "
+                       f"worker processes, {wall:.1f} s wall; FLOPs counted as 4·D per allowed pair",
+                seconds=wall)
+
+
+# ---------------------------------------------------------------- GPU legs
+
+def decode_bytes(c) -> int:
+    lens = c["cache_seqlens"].long()
+    Hkv, D = c["k_pool"].shape[2], c["k_pool"].shape[3]
+    es = c["k_pool"].element_size()
+    kv = int(lens.sum()) * Hkv * D * 2 * es
+    page = c["page_size"]
+    bt = int(((lens + page - 1) // page).sum()) * 4
+    q = c["q"].numel() * c["q"].element_size()
+    return kv + 2 * q + bt + 4 * lens.numel()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=128)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one leg only (for profiling); the JSON line is still printed")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_forward_fa_amd as fa
+    from exact_attention_forward_fa_amd import inputs
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    # inputs (CPU, seeded), then resident on the GPU
+    run_p = args.only in (None, "prefill")
+    run_d = args.only in (None, "decode")
+    t = time.perf_counter()
+    pc = inputs.case("c3_causal")
+    dc = inputs.case("c5_paged") if run_d else None
+    log(f"inputs generated in {time.perf_counter() - t:.1f} s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        cpu = cpu_baseline(pc, args.cpu_heads, workers)
+        log(f"cpu baseline: {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s on {workers} cores")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (pc[n].to(dev) for n in ("q", "k", "v"))
+    B, S, H, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    if run_d:
+        dq = dc["q"].to(dev)
+        kp, vp = dc["k_pool"].to(dev), dc["v_pool"].to(dev)
+        bt, lens = dc["block_table"].to(dev), dc["cache_seqlens"].to(dev)
+        ns = dc["num_splits"]
+        dB, _, dH, dD = dc["q"].shape
+        ws = torch.empty(fa.kvcache_workspace_size(dB, 1, dH, dD, ns), dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(dq)
+        dlse = torch.empty((dB, dH, 1), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if run_p:
+            if ev: ev[0].record()
+            fa.fwd(q, k, v, causal=True, out=out, lse=lse)
+            if ev: ev[1].record()
+        if run_d:
+            if ev: ev[2].record()
+            fa.fwd_kvcache(dq, kp, vp, lens, block_table=bt, num_splits=ns, workspace=ws, out=dout, lse=dlse)
+            if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = [e[0].elapsed_time(e[1]) for e in evs] if run_p else [float("nan")]
+    d_ms = [e[2].elapsed_time(e[3]) for e in evs] if run_d else [float("nan")]
+    p_mean = sum(p_ms) / len(p_ms)
+    d_mean = sum(d_ms) / len(d_ms)
+    p_flops = 4 * D * causal_pairs(S, S) * B * H
+    tflops = p_flops / (p_mean * 1e-3) / 1e12
+    d_bytes = decode_bytes(dc) if run_d else 0
+    gbs = d_bytes / (d_mean * 1e-3) / 1e9
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read + {n} bytes written")
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("prefill_source_sha") == kernel_source_hash():
+            traffic = tr["prefill_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    line = {
+        "metric": "attn fwd TFLOP/s (causal, B4 S4096 H32 D64 fp16) + paged decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill B=4 Sq=Sk=4096 Hq=Hkv=32 D=64 fp16 (N(0,1), seed 1003) + paged "
+                        "split-KV decode B=64 Sq=1 Hq=32 Hkv=8 D=128 bf16, len~U[1024,16384], 256-token "
+                        "pages, permuted block table, 16 splits + LSE combine (seed 1005)",
+            "global_batch": B, "seq_len": S, "parallelism": "single GPU",
+        },
+        "prefill": {"ms_mean": round(p_mean, 5), "ms_min": round(min(p_ms), 5), "flops": p_flops,
+                    "tflops": round(tflops, 2)},
+        "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms_mean": round(d_mean, 5),
+                   "ms_min": round(min(d_ms), 5), "bytes": d_bytes, "dtype": "bf16",
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": None if cpu is None else {kk: cpu[kk] for kk in ("value", "unit", "cores", "kind", "sample")},
+    }
+    if cpu is not None:
+        line["cpu_baseline"]["value"] = round(cpu["value"], 6)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

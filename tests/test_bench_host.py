@@ -1,0 +1,26 @@
+"""Host-side pieces of bench.py (no GPU): FLOP and byte accounting."""
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from exact_attention_forward_fa_amd import inputs
+from oracle import ref
+
+
+@pytest.mark.parametrize("sq,sk", [(4096, 4096), (100, 37), (37, 100), (1, 50), (5, 5), (1, 1), (300, 299)])
+def test_causal_pair_count_matches_oracle_mask(sq, sk):
+    assert bench.causal_pairs(sq, sk) == int(ref.allowed_mask(np.arange(sq), sq, sk, True).sum())
+
+
+def test_metric_flops():
+    # 4 * D per allowed pair, B*H heads: the causal B4 S4096 H32 D64 workload
+    assert 4 * 64 * bench.causal_pairs(4096, 4096) * 4 * 32 == 274945015808
+
+
+def test_decode_bytes_counts_each_cached_token_once():
+    pc = inputs.paged_cache(3, 1, 8, 2, 64, torch.bfloat16, seed=1, page_size=16, lengths=[5, 16, 40])
+    c = dict(q=pc.q, k_pool=pc.k_pool, cache_seqlens=pc.cache_seqlens, page_size=16)
+    kv = (5 + 16 + 40) * 2 * 64 * 2 * 2
+    assert bench.decode_bytes(c) == kv + 2 * pc.q.numel() * 2 + (1 + 1 + 3) * 4 + 3 * 4
