@@ -73,6 +73,19 @@ hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s
 hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s);
 hipError_t launch_combine(Dtype dt, const CombineParams& p, hipStream_t s);
 
-constexpr int kPrefillBlockM = 128;   // query rows per prefill workgroup
+// Prefill workgroup shape per head dim: NW waves, each owning RB blocks of 32 query rows.
+#ifndef FA_PREFILL_NW64
+#define FA_PREFILL_NW64 8
+#endif
+#ifndef FA_PREFILL_RB64
+#define FA_PREFILL_RB64 1
+#endif
+#ifndef FA_PREFILL_NW128
+#define FA_PREFILL_NW128 8
+#endif
+#ifndef FA_PREFILL_RB128
+#define FA_PREFILL_RB128 1
+#endif
+constexpr int kPrefillBlockM = 256;   // query rows per prefill workgroup (NW * 32 * RB)
 
 }  // namespace fa

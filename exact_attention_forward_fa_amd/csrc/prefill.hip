@@ -28,25 +28,36 @@
 
 namespace fa {
 
+constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
+
+// Head dims from which the ping-pong kernel is used.  With D = 64 the softmax
+// phase outweighs the MFMA phase and a single wave per SIMD cannot issue VALU
+// work fast enough, so the 4-waves-per-SIMD kernel is faster there.
+#ifndef FA_PREFILL_PINGPONG_MIN_D
+#define FA_PREFILL_PINGPONG_MIN_D 128
+#endif
+#ifndef FA_PREFILL_WAVES_PER_EU
+#define FA_PREFILL_WAVES_PER_EU 2    // register budget: 256 VGPRs+AGPRs per wave
+#endif
+
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-// 16-byte chunk c of tile row r is stored at chunk kswz / vswz (bank-conflict
-// free for the K row reads and the transposing V reads respectively).
-template <int D>
-__device__ __forceinline__ int kswz(int r, int c) {
-  return D == 64 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
-}
-template <int D>
-__device__ __forceinline__ int vswz(int r, int c) {
-  return D == 64 ? (c ^ (((r >> 1) & 1) << 2)) : (c ^ ((r & 3) << 2));
-}
+// LDS row strides (elements) of the K and V tiles.  Padding instead of an XOR
+// swizzle keeps every LDS read at "one base register + immediate offset":
+//  * K rows of 2D+16 bytes: the 16 lanes of a 16-byte K read hit 16 different
+//    rows, whose starts then fall on 16 distinct 16-byte bank groups;
+//  * V rows of 2D+64 bytes: a transposing read covers 4 rows x 64 bytes per 32
+//    lanes, and the 64-byte row offsets map those rows to 4 disjoint bank ranges.
+template <int D> constexpr int k_stride() { return D + 8; }
+template <int D> constexpr int v_stride() { return D + 32; }
 
-template <class E, int D, int BN, int NW, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
+template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_PREFILL_WAVES_PER_EU)))
+void prefill_kernel(PrefillParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
   using V2 = typename E::V2;
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * 32 * RB;        // query rows per workgroup
   constexpr int CH = D / 8;               // 16-byte chunks per row
   constexpr int KB = BN / 32;             // 32-key blocks per tile
   constexpr int DC = D / 16;              // contraction steps of Q K^T
@@ -56,9 +67,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
   static_assert(LOADS * NT == BN * CH, "tile must split evenly over the workgroup");
   constexpr bool PLAIN = !SOFTCAP && !ALIBI;
 
-  __shared__ __attribute__((aligned(16))) T smem[2][2][BN * D];   // [buffer][K, V][row * D]
+  constexpr int KS = k_stride<D>(), VS = v_stride<D>();
+  __shared__ __attribute__((aligned(16))) T ksm[2][BN * KS];   // K tiles, double-buffered
+  __shared__ __attribute__((aligned(16))) T vsm[2][BN * VS];   // V tiles
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
 
   // ---- workgroup -> (batch, query head, query tile); heads are spread over the
   // 8 XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
@@ -97,36 +111,50 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
   const int t_lo = kv_lo / BN;
   const int t_hi = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : t_lo;
 
-  // ---- this lane's query row and its allowed key interval [j_lo, j_hi]
-  const int qrow = m0 + wave * 32 + l32;
-  const bool row_ok = qrow < sq;
-  const int ip = qrow + shift;
-  int j_lo = 0, j_hi = sk - 1;
-  if (p.wl >= 0) j_lo = max(j_lo, ip - p.wl);
-  if (p.causal) j_hi = min(j_hi, ip);
-  if (p.wr >= 0) j_hi = min(j_hi, ip + p.wr);
-
-  // the same bounds over the wave's rows, to classify tiles as empty / full / edge
-  const int w0 = m0 + wave * 32, w1 = min(w0 + 32, sq) - 1;
-  const bool wave_live = w0 < sq;
-  int lo_min = 0, lo_max = 0, hi_min = sk - 1, hi_max = sk - 1;
-  if (p.wl >= 0) { lo_min = max(0, w0 + shift - p.wl); lo_max = max(0, w1 + shift - p.wl); }
-  if (p.causal) { hi_min = min(hi_min, w0 + shift); hi_max = min(hi_max, w1 + shift); }
-  if (p.wr >= 0) { hi_min = min(hi_min, w0 + shift + p.wr); hi_max = min(hi_max, w1 + shift + p.wr); }
-
-  // ---- Q operand (B of S^T = K Q^T): lane holds row qrow, d = 16*dc + 8*hi .. +7
-  V8 qr[DC];
+  // ---- the wave owns RB blocks of 32 query rows; block rb covers rows
+  // m0 + rb*(NW*32) + wave*32 + [0, 32), so at the causal diagonal every wave
+  // holds one block from each half of the tile and the waves stay balanced.
+  int qrow[RB], j_lo[RB], j_hi[RB];
+  bool row_ok[RB];
+  int lo_min[RB], lo_max[RB], hi_min[RB], hi_max[RB];   // bounds over the block's rows (scalar)
+  bool blk_live[RB];
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    if (row_ok) qr[dc] = *(const V8*)(qp + (int64_t)qrow * p.q_ss + dc * 16 + hi * 8);
-    else qr[dc] = V8{};
+  for (int rb = 0; rb < RB; ++rb) {
+    const int w0 = m0 + rb * NW * 32 + wave * 32;
+    qrow[rb] = w0 + l32;
+    row_ok[rb] = qrow[rb] < sq;
+    const int ip = qrow[rb] + shift;
+    j_lo[rb] = 0; j_hi[rb] = sk - 1;
+    if (p.wl >= 0) j_lo[rb] = max(j_lo[rb], ip - p.wl);
+    if (p.causal) j_hi[rb] = min(j_hi[rb], ip);
+    if (p.wr >= 0) j_hi[rb] = min(j_hi[rb], ip + p.wr);
+    const int w1 = min(w0 + 32, sq) - 1;
+    blk_live[rb] = w0 < sq;
+    lo_min[rb] = 0; lo_max[rb] = 0; hi_min[rb] = sk - 1; hi_max[rb] = sk - 1;
+    if (p.wl >= 0) { lo_min[rb] = max(0, w0 + shift - p.wl); lo_max[rb] = max(0, w1 + shift - p.wl); }
+    if (p.causal) { hi_min[rb] = min(hi_min[rb], w0 + shift); hi_max[rb] = min(hi_max[rb], w1 + shift); }
+    if (p.wr >= 0) { hi_min[rb] = min(hi_min[rb], w0 + shift + p.wr); hi_max[rb] = min(hi_max[rb], w1 + shift + p.wr); }
+    if (lo_min[rb] > hi_max[rb]) blk_live[rb] = false;   // no row of the block sees any key
   }
 
-  float slope_l2 = 0.f, ipf = 0.f;
-  if constexpr (ALIBI) { slope_l2 = p.alibi[hq] * kLog2e; ipf = (float)ip; }
+  // ---- Q operand (B of S^T = K Q^T): lane holds row qrow, d = 16*dc + 8*hi .. +7
+  V8 qr[RB][DC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      if (row_ok[rb]) qr[rb][dc] = *(const V8*)(qp + (int64_t)qrow[rb] * p.q_ss + dc * 16 + hi * 8);
+      else qr[rb][dc] = V8{};
+    }
+
+  float slope_l2 = 0.f, ipf[RB];
+  if constexpr (ALIBI) slope_l2 = p.alibi[hq] * kLog2e;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) ipf[rb] = (float)(qrow[rb] + shift);
   const float sl2 = p.scale * kLog2e;
   const float cap_l2 = p.softcap * kLog2e;                 // softcap in log2 units
   const float cap_in = 2.f * p.scale * kLog2e / (SOFTCAP ? p.softcap : 1.f);
+  const float mult = PLAIN ? sl2 : 1.f;
 
   // ---- global -> register staging of one K/V tile (rows past sk are clamped to a
   // real row; their scores are masked, so their values only ever meet p = 0)
@@ -145,20 +173,147 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
-      *(u32x4*)(&smem[buf][0][r * D + kswz<D>(r, c) * 8]) = kst[i];
-      *(u32x4*)(&smem[buf][1][r * D + vswz<D>(r, c) * 8]) = vst[i];
+      *(u32x4*)(&ksm[buf][r * KS + c * 8]) = kst[i];
+      *(u32x4*)(&vsm[buf][r * VS + c * 8]) = vst[i];
     }
   };
 
-  f32x16 o[DB];
+  f32x16 o[RB][DB];
+  // Running row max m (log2 units) and row sums over this lane's keys (the other
+  // half is added at the end): l of the rounded P that feeds the P V product
+  // (normalises out, so out is an exact convex combination of the rounded
+  // weights) and lx of the unrounded fp32 P (gives an lse free of P rounding).
+  // The max is lazy: O, l, lx are rescaled only when some row's max grows by
+  // more than kTau (P then stays below 2^kTau), which leaves the result exact.
+  float m[RB], l[RB], lx[RB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = kNegInf;     // running row max, log2 units
-  // running row sums over this lane's keys (the other half is added at the end):
-  // l of the rounded P that feeds the P V product (normalises out, so out is an
-  // exact convex combination of the rounded weights), lx of the unrounded fp32 P
-  // (gives an lse free of the P rounding)
-  float l = 0.f, lx = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[rb][db] = f32x16{};
+    m[rb] = kNegInf; l[rb] = 0.f; lx[rb] = 0.f;
+  }
+
+  // One tile for the wave's RB row blocks.  Mask arithmetic runs only when the
+  // tile straddles a mask edge for this wave (a uniform branch); a single body
+  // keeps register pressure at one copy of the tile state.
+  auto step = [&](bool edge, int j0, const T* Ks, const T* Vs) {
+    // S^T = K Q^T: s[rb][kb][r] is key j0 + 32kb + 8(r/4) + 4hi + (r%4) of row qrow[rb];
+    // each K operand read from LDS feeds the RB row blocks
+    f32x16 s[RB][KB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[rb][kb] = f32x16{};
+    const T* kbase = Ks + l32 * KS + hi * 8;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const V8 a = *(const V8*)(kbase + kb * 32 * KS + dc * 16);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = E::mfma32(a, qr[rb][dc], s[rb][kb]);
+      }
+
+    bool grow = false;
+    float m_new[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if constexpr (!PLAIN) {
+        const float dj0 = (float)(j0 + 4 * hi) - ipf[rb];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = s[rb][kb][r];
+            if constexpr (SOFTCAP) {
+              const float e = exp2_fast(x * cap_in);
+              x = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
+            } else {
+              x *= sl2;
+            }
+            if constexpr (ALIBI) {
+              const float dist = dj0 + (float)(kb * 32 + (r >> 2) * 8 + (r & 3));
+              x = fmaf(-slope_l2, fabsf(dist), x);
+            }
+            s[rb][kb][r] = x;
+          }
+      }
+      if (edge) {
+        const int jb = j0 + 4 * hi;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = jb + kb * 32 + (r >> 2) * 8 + (r & 3);
+            if (j < j_lo[rb] || j > j_hi[rb]) s[rb][kb][r] = kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[rb][kb][r], s[rb][kb][r + 1]));
+      mx = max_halves(mx) * mult;
+      m_new[rb] = fmaxf(m[rb], mx);
+      grow |= m_new[rb] > m[rb] + kTau;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float alpha = m_new[rb] == kNegInf ? 1.f : exp2_fast(m[rb] - m_new[rb]);
+        m[rb] = m_new[rb];
+        l[rb] *= alpha;
+        lx[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+      }
+    }
+
+    // P = exp2(s - m), rounded for the P V product
+    V2 pk[RB][KB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float m_use = m[rb] == kNegInf ? 0.f : m[rb];
+      float ls = 0.f, lxs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = exp2_fast(fmaf(s[rb][kb][r], mult, -m_use));
+          const float p1 = exp2_fast(fmaf(s[rb][kb][r + 1], mult, -m_use));
+          pk[rb][kb][r >> 1] = E::pack(p0, p1);
+          ls = E::sum2(pk[rb][kb][r >> 1], ls);
+          lxs += p0 + p1;
+        }
+      l[rb] += ls;
+      lx[rb] += lxs;
+    }
+
+    // O^T += V^T P^T over 16-key chunks; each V operand read feeds the RB blocks.
+    // Transposing read: lane (g = lane % 16) of each 16-lane group addresses row
+    // 16c + 4hi + g/4 (+8 for the second half), columns 32db + 16((lane/16)%2) + 4(g%4).
+    const T* vbase = Vs + (hi * 4 + ((lane & 15) >> 2)) * VS + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+#pragma unroll
+    for (int c = 0; c < BN / 16; ++c) {
+      const int kb = c >> 1, c2 = c & 1;
+      V8 bop[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bop[rb][2 * e] = pk[rb][kb][4 * c2 + e][0];
+          bop[rb][2 * e + 1] = pk[rb][kb][4 * c2 + e][1];
+        }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 x0 = lds_read_tr16(vbase + c * 16 * VS + db * 32);
+        const i16x4 x1 = lds_read_tr16(vbase + (c * 16 + 8) * VS + db * 32);
+        const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mfma32(a, bop[rb], o[rb][db]);
+      }
+    }
+  };
 
   if (t_lo < t_hi) {
     gload(t_lo);
@@ -170,89 +325,204 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
     const int buf = (t - t_lo) & 1;
     if (t + 1 < t_hi) gload(t + 1);
     const int j0 = t * BN;
-    const bool empty = !wave_live || lo_min > hi_max || j0 + BN - 1 < lo_min || j0 > hi_max;
-    if (!empty) {
-      const bool full = j0 >= lo_max && j0 + BN - 1 <= hi_min;
-      const T* Ks = smem[buf][0];
-      const T* Vs = smem[buf][1];
+    bool any_live = false, all_full = true;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool live = blk_live[rb] && j0 + BN - 1 >= lo_min[rb] && j0 <= hi_max[rb];
+      any_live |= live;
+      all_full &= live && j0 >= lo_max[rb] && j0 + BN - 1 <= hi_min[rb];
+    }
+    if (any_live) {
+      step(!all_full, j0, ksm[buf], vsm[buf]);
+    }
+    if (t + 1 < t_hi) swrite(buf ^ 1);
+    __syncthreads();
+  }
 
-      // S^T = K Q^T : s[kb][r] is key j0 + 32kb + 8(r/4) + 4hi + (r%4) of row qrow
-      f32x16 s[KB];
+  // ---- epilogue: out = O / l, lse = ln(sum exp(scores)) = (m + log2 lx) * ln 2
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = f32x16{};
-        const int r = kb * 32 + l32;
+  for (int rb = 0; rb < RB; ++rb) {
+    const float lt = sum_halves(l[rb]);
+    const float lxt = sum_halves(lx[rb]);
+    if (row_ok[rb]) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      T* orow = op + (int64_t)qrow[rb] * p.o_ss;
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const V8 a = *(const V8*)(Ks + r * D + kswz<D>(r, dc * 2 + hi) * 8);
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          V2 a = E::pack(o[rb][db][4 * gq] * inv, o[rb][db][4 * gq + 1] * inv);
+          V2 c = E::pack(o[rb][db][4 * gq + 2] * inv, o[rb][db][4 * gq + 3] * inv);
+          u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+          *(u32x2*)(orow + db * 32 + gq * 8 + hi * 4) = w;
+        }
+      if (hi == 0) lp[qrow[rb]] = lxt > 0.f ? (m[rb] + __log2f(lxt)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant.  The 8 waves form two groups (waves w and w+4 share a
+// SIMD).  Each wave alternates a GEMM phase (Q K^T of tile j on MFMA, then
+// P V of tile j-1) and a softmax phase (scores of tile j -> P on VALU and the
+// transcendental unit), and group 1 runs one phase behind group 0, so on every
+// SIMD one wave keeps the matrix cores busy while the other does the
+// exponentials.  Phases end at workgroup barriers; K/V tiles rotate through
+// three LDS stages, each wave staging its share of tile j+1 during GEMM phase
+// j-1 and storing it during GEMM phase j.
+// ---------------------------------------------------------------------------
+template <class E, int D, int BN, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FA_PREFILL_WAVES_PER_EU)))
+void prefill_pp_kernel(PrefillParams p) {
+  using T = typename E::T;
+  using V8 = typename E::V8;
+  using V2 = typename E::V2;
+  constexpr int NW = 8;
+  constexpr int BM = NW * 32;
+  constexpr int CH = D / 8;
+  constexpr int KB = BN / 32;
+  constexpr int DC = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int LOADS = BN * CH / NT;
+  static_assert(LOADS * NT == BN * CH, "tile must split evenly over the workgroup");
+  constexpr bool PLAIN = !SOFTCAP && !ALIBI;
+  constexpr int KS = k_stride<D>(), VS = v_stride<D>();
+  __shared__ __attribute__((aligned(16))) T ksm[3][BN * KS];
+  __shared__ __attribute__((aligned(16))) T vsm[3][BN * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+
+  int id = blockIdx.x;
+  if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
+  const int head = id / p.n_qtiles;
+  const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);
+  const int b = head / p.Hq, hq = head - b * p.Hq;
+  const int hk = hq / p.group;
+
+  int sq = p.Sq, sk = p.Sk, qbase = 0, kbase = 0;
+  if (p.cu_seqlens_q) {
+    qbase = p.cu_seqlens_q[b];
+    sq = p.cu_seqlens_q[b + 1] - qbase;
+    kbase = p.cu_seqlens_k[b];
+    sk = p.cu_seqlens_k[b + 1] - kbase;
+  }
+  const int m0 = qt * BM;
+  if (m0 >= sq) return;
+
+  const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
+  const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
+  const T* kp = (const T*)p.k + bq * p.k_sb + (int64_t)kbase * p.k_ss + (int64_t)hk * p.k_sh;
+  const T* vp = (const T*)p.v + bq * p.v_sb + (int64_t)kbase * p.v_ss + (int64_t)hk * p.v_sh;
+  T* op = (T*)p.out + bq * p.o_sb + (int64_t)qbase * p.o_ss + (int64_t)hq * p.o_sh;
+  float* lp = p.lse + bq * p.lse_sb + (int64_t)hq * p.lse_sh + qbase;
+
+  const int shift = sk - sq;
+  const int ip_first = m0 + shift, ip_last = min(m0 + BM, sq) - 1 + shift;
+  int kv_lo = 0, kv_hi = sk;
+  if (p.wl >= 0) kv_lo = max(0, ip_first - p.wl);
+  if (p.causal) kv_hi = min(kv_hi, ip_last + 1);
+  if (p.wr >= 0) kv_hi = min(kv_hi, ip_last + p.wr + 1);
+  const int t_lo = kv_lo / BN;
+  const int n_t = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN - t_lo : 0;
+
+  const int w0 = m0 + wave * 32;
+  const int qrow = w0 + l32;
+  const bool row_ok = qrow < sq;
+  const int ip = qrow + shift;
+  int j_lo = 0, j_hi = sk - 1;
+  if (p.wl >= 0) j_lo = max(j_lo, ip - p.wl);
+  if (p.causal) j_hi = min(j_hi, ip);
+  if (p.wr >= 0) j_hi = min(j_hi, ip + p.wr);
+  const int w1 = min(w0 + 32, sq) - 1;
+  int lo_max = 0, hi_min = sk - 1;
+  if (p.wl >= 0) lo_max = max(0, w1 + shift - p.wl);
+  if (p.causal) hi_min = min(hi_min, w0 + shift);
+  if (p.wr >= 0) hi_min = min(hi_min, w0 + shift + p.wr);
+
+  V8 qr[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc) {
+    if (row_ok) qr[dc] = *(const V8*)(qp + (int64_t)qrow * p.q_ss + dc * 16 + hi * 8);
+    else qr[dc] = V8{};
+  }
+  float slope_l2 = 0.f;
+  if constexpr (ALIBI) slope_l2 = p.alibi[hq] * kLog2e;
+  const float ipf = (float)ip;
+  const float sl2 = p.scale * kLog2e;
+  const float cap_l2 = p.softcap * kLog2e;
+  const float cap_in = 2.f * p.scale * kLog2e / (SOFTCAP ? p.softcap : 1.f);
+  const float mult = PLAIN ? sl2 : 1.f;
+
+  u32x4 kst[LOADS], vst[LOADS];
+  auto gload = [&](int i) {
+    const int j0 = (t_lo + i) * BN;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = tid + u * NT, r = cid / CH, c = cid - r * CH;
+      const int j = min(j0 + r, sk - 1);
+      kst[u] = *(const u32x4*)(kp + (int64_t)j * p.k_ss + c * 8);
+      vst[u] = *(const u32x4*)(vp + (int64_t)j * p.v_ss + c * 8);
+    }
+  };
+  auto swrite = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int cid = tid + u * NT, r = cid / CH, c = cid - r * CH;
+      *(u32x4*)(&ksm[st][r * KS + c * 8]) = kst[u];
+      *(u32x4*)(&vsm[st][r * VS + c * 8]) = vst[u];
+    }
+  };
+  // LDS writes of this wave complete, then all 8 waves meet
+  auto barrier = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = kNegInf, l = 0.f, lx = 0.f;
+  f32x16 s[KB];
+  V2 pk[KB][8];
+
+  if (n_t > 0) { gload(0); swrite(0); }
+  if (n_t > 1) { gload(1); swrite(1); }
+  if (n_t > 2) gload(2);
+  barrier();
+  if (grp == 1) barrier();                 // group 1 runs one phase behind
+
+  int st_q = 0;                            // stage of tile j (K read by this GEMM phase)
+  for (int j = 0; j <= n_t; ++j) {
+    const int st_p = st_q == 0 ? 2 : st_q - 1;      // stage of tile j-1 (V read by P V)
+    const int st_w = st_q == 2 ? 0 : st_q + 1;      // stage of tile j+1 (written now)
+    // ---------------- GEMM phase j
+    __builtin_amdgcn_s_setprio(1);
+    if (j >= 1 && j + 1 < n_t) swrite(st_w);
+    if (j >= 1 && j + 2 < n_t) gload(j + 2);
+    if (j < n_t) {
+      const T* kb_ = ksm[st_q] + l32 * KS + hi * 8;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        if (D > 64 && (dc & 1) == 0) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const V8 a = *(const V8*)(kb_ + kb * 32 * KS + dc * 16);
           s[kb] = E::mfma32(a, qr[dc], s[kb]);
         }
       }
-
-      // score transforms into log2 units (the plain path folds the scale into exp2)
-      if constexpr (!PLAIN) {
-        const float dj0 = (float)(j0 + 4 * hi) - ipf;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = s[kb][r];
-            if constexpr (SOFTCAP) {
-              const float e = exp2_fast(x * cap_in);
-              x = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
-            } else {
-              x *= sl2;
-            }
-            if constexpr (ALIBI) {
-              const float dist = dj0 + (float)(kb * 32 + (r >> 2) * 8 + (r & 3));
-              x = fmaf(-slope_l2, fabsf(dist), x);
-            }
-            s[kb][r] = x;
-          }
-      }
-      if (!full) {
-        const int jb = j0 + 4 * hi;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = jb + kb * 32 + (r >> 2) * 8 + (r & 3);
-            if (j < j_lo || j > j_hi) s[kb][r] = kNegInf;
-          }
-      }
-
-      // online softmax
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = max_halves(mx);
-      const float mult = PLAIN ? sl2 : 1.f;
-      const float m_new = fmaxf(m, mx * mult);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
-      V2 pk[KB][8];
-      float ls = 0.f, lxs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_fast(fmaf(s[kb][r], mult, -m_use));
-          const float p1 = exp2_fast(fmaf(s[kb][r + 1], mult, -m_use));
-          pk[kb][r >> 1] = E::pack(p0, p1);
-          ls = E::sum2(pk[kb][r >> 1], ls);
-          lxs += p0 + p1;
-        }
-      l = fmaf(l, alpha, ls);
-      lx = fmaf(lx, alpha, lxs);
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-
-      // O^T += V^T P^T over 16-key chunks
+    }
+    if (j >= 1) {
+      const T* vb_ = vsm[st_p] + (hi * 4 + ((lane & 15) >> 2)) * VS + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 #pragma unroll
       for (int c = 0; c < BN / 16; ++c) {
+        // keep the operand reads of one 16-key chunk in flight at a time (bounds registers)
+        if (D > 64) __builtin_amdgcn_sched_barrier(0);
         const int kb = c >> 1, c2 = c & 1;
         V8 bop;
 #pragma unroll
@@ -260,24 +530,85 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
           bop[2 * e] = pk[kb][4 * c2 + e][0];
           bop[2 * e + 1] = pk[kb][4 * c2 + e][1];
         }
-        const int g = lane & 15;
-        const int row = c * 16 + hi * 4 + (g >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int col = db * 32 + ((lane >> 4) & 1) * 16 + (g & 3) * 4;
-          const int cc = col >> 3, co = col & 7;
-          const i16x4 x0 = lds_read_tr16(Vs + row * D + vswz<D>(row, cc) * 8 + co);
-          const i16x4 x1 = lds_read_tr16(Vs + (row + 8) * D + vswz<D>(row + 8, cc) * 8 + co);
-          const i16x8 xa = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = E::mfma32(__builtin_bit_cast(V8, xa), bop, o[db]);
+          const i16x4 x0 = lds_read_tr16(vb_ + c * 16 * VS + db * 32);
+          const i16x4 x1 = lds_read_tr16(vb_ + (c * 16 + 8) * VS + db * 32);
+          const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = E::mfma32(a, bop, o[db]);
         }
       }
     }
-    if (t + 1 < t_hi) swrite(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
+    barrier();
+    if (j == n_t) break;
+    // ---------------- softmax phase j
+    const int j0 = (t_lo + j) * BN;
+    const bool edge = !(j0 >= lo_max && j0 + BN - 1 <= hi_min);
+    if constexpr (!PLAIN) {
+      const float dj0 = (float)(j0 + 4 * hi) - ipf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kb][r];
+          if constexpr (SOFTCAP) {
+            const float e = exp2_fast(x * cap_in);
+            x = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
+          } else {
+            x *= sl2;
+          }
+          if constexpr (ALIBI) {
+            const float dist = dj0 + (float)(kb * 32 + (r >> 2) * 8 + (r & 3));
+            x = fmaf(-slope_l2, fabsf(dist), x);
+          }
+          s[kb][r] = x;
+        }
+    }
+    if (edge) {
+      const int jb = j0 + 4 * hi;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jj = jb + kb * 32 + (r >> 2) * 8 + (r & 3);
+          if (jj < j_lo || jj > j_hi) s[kb][r] = kNegInf;
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+    mx = max_halves(mx) * mult;
+    const float m_new = fmaxf(m, mx);
+    if (__any(m_new > m + kTau)) {
+      const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
+      m = m_new;
+      l *= alpha;
+      lx *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    const float m_use = m == kNegInf ? 0.f : m;
+    float ls = 0.f, lxs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_fast(fmaf(s[kb][r], mult, -m_use));
+        const float p1 = exp2_fast(fmaf(s[kb][r + 1], mult, -m_use));
+        pk[kb][r >> 1] = E::pack(p0, p1);
+        ls = E::sum2(pk[kb][r >> 1], ls);
+        lxs += p0 + p1;
+      }
+    l += ls;
+    lx += lxs;
+    barrier();
+    st_q = st_w;
   }
+  if (grp == 0) barrier();                 // matches group 1's initial offset
 
-  // ---- epilogue: out = O / l, lse = ln(sum exp(scores)) = (m + log2 lx) * ln 2
   const float lt = sum_halves(l);
   const float lxt = sum_halves(lx);
   if (row_ok) {
@@ -296,12 +627,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillParams p) {
   }
 }
 
+// Tile shapes: 8 waves of one 32-row block each, i.e. 256 query rows per
+// workgroup and 64-key tiles, for both head dims.  (RB = 2 blocks per wave
+// shares every K/V operand read between two MFMAs but needs more than the
+// 256-register budget of two waves per SIMD.)
+template <int D> struct Shape;
+template <> struct Shape<64> { static constexpr int NW = FA_PREFILL_NW64, RB = FA_PREFILL_RB64, BN = 64; };
+template <> struct Shape<128> { static constexpr int NW = FA_PREFILL_NW128, RB = FA_PREFILL_RB128, BN = 64; };
+
 template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
-  constexpr int NW = 4, BN = 64;
-  static_assert(NW * 32 == kPrefillBlockM, "");
+  using S = Shape<D>;
+  static_assert(S::NW * 32 * S::RB == kPrefillBlockM, "workgroup row count must match the host grid");
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
-  hipLaunchKernelGGL((prefill_kernel<E, D, BN, NW, SC, AL>), dim3(grid), dim3(NW * 64), 0, s, p);
+  if (D >= FA_PREFILL_PINGPONG_MIN_D)
+    hipLaunchKernelGGL((prefill_pp_kernel<E, D, 64, SC, AL>), dim3(grid), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, S::NW, S::RB, SC, AL>), dim3(grid), dim3(S::NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
