@@ -48,13 +48,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const float inv = W > 0.f ? 1.f / W : 0.f;
 
   T* orow = (T*)p.out + b * p.o_sb + s * p.o_ss + h * p.o_sh;
-  for (int d = lane; d < p.D; d += 64) {
-    float acc = 0.f;
+  // Each lane owns up to kCombineCols columns; the loads of all splits are issued
+  // before they are consumed.  Splits with weight 0 (empty, lse = -inf) are
+  // never read, so their partials may hold anything.
+  constexpr int kCombineCols = 4;
+  for (int d0 = 0; d0 < p.D; d0 += 64 * kCombineCols) {
+    float acc[kCombineCols] = {};
     for (int sp = 0; sp < p.num_splits; ++sp) {
       const float ws = __shfl(w, sp, 64);
-      if (ws != 0.f) acc = fmaf(ws, opp[d * p.op_sd + sp * p.op_sn], acc);
+      if (ws == 0.f) continue;                       // uniform across the wave
+      const float* src = opp + sp * p.op_sn;
+#pragma unroll
+      for (int c = 0; c < kCombineCols; ++c) {
+        const int d = d0 + c * 64 + lane;
+        if (d < p.D) acc[c] = fmaf(ws, src[d * p.op_sd], acc[c]);
+      }
     }
-    orow[d] = E::from_f32(acc * inv);
+#pragma unroll
+    for (int c = 0; c < kCombineCols; ++c) {
+      const int d = d0 + c * 64 + lane;
+      if (d < p.D) orow[d] = E::from_f32(acc[c] * inv);
+    }
   }
   if (p.lse && lane == 0)
     p.lse[b * p.l_sb + s * p.l_ss + h * p.l_sh] = W > 0.f ? M + __logf(W) : kNegInf;

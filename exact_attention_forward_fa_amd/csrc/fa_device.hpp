@@ -30,6 +30,9 @@ struct F16 {
   static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
   // round-to-nearest-even pack of two floats (v_cvt_pk_f16_f32)
   static __device__ __forceinline__ V2 pack(float a, float b) {
     V2 r; r[0] = (T)a; r[1] = (T)b; return r;
@@ -49,6 +52,9 @@ struct BF16 {
   typedef bf16x2 V2;
   static __device__ __forceinline__ f32x16 mfma32(V8 a, V8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   // round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
   static __device__ __forceinline__ V2 pack(float a, float b) {
