@@ -187,7 +187,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t fa_kvcache_workspace_size(int B, int Sq, int Hq, int D, int num_splits) {
   if (B <= 0 || Sq <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0) return 0;
   const size_t rows = (size_t)B * Sq * Hq * num_splits;
-  return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float));
+  return align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)) + align256((size_t)B * 2 * sizeof(int));
 }
 
 int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits) {
@@ -232,16 +232,27 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
   if (workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
 
+  // the decode schedule numbers work items (b, split, kv head) and rounds in int
+  if ((int64_t)B * ns * Hkv > (int64_t)1 << 30)
+    return fail(FA_ERR_UNSUPPORTED, "B*num_splits*Hkv = %lld work items; at most 2^30 are built",
+                (long long)B * ns * Hkv);
+
   const size_t rows = (size_t)B * Sq * Hq * ns;
-  float* op = static_cast<float*>(workspace);
-  float* lp = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * D * sizeof(float)));
+  char* ws = static_cast<char*>(workspace);
+  float* op = reinterpret_cast<float*>(ws);
+  float* lp = reinterpret_cast<float*>(ws + align256(rows * D * sizeof(float)));
+  int2* order = reinterpret_cast<int2*>(ws + align256(rows * D * sizeof(float)) + align256(rows * sizeof(float)));
 
   fa::DecodeParams d{};
   d.q = q; d.k = k_cache; d.v = v_cache;
+  // the decode kernel may read row 0 of the cache past the end of its work; an
+  // empty cache (every sequence of length 0) gets q as a stand-in
+  if (num_blocks_or_smax == 0) { d.k = q; d.v = q; }
   d.cache_seqlens = cache_seqlens;
   d.block_table = block_table;
   d.bt_stride = block_table_stride;
   d.page_size = block_table ? page_size : num_blocks_or_smax;
+  d.cache_rows = (int64_t)num_blocks_or_smax * (block_table ? page_size : B);
   d.log2_page = -1;
   if (block_table && (page_size & (page_size - 1)) == 0) {
     int lg = 0;
@@ -249,6 +260,7 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
     d.log2_page = lg;
   }
   d.out_partial = op; d.lse_partial = lp;
+  d.order = B > 64 ? order : nullptr;   // up to 64 sequences are ranked inside the decode kernel
   d.B = B; d.Sq = Sq; d.Hq = Hq; d.Hkv = Hkv; d.group = Hq / Hkv;
   d.num_splits = ns;
   d.scale = scale;

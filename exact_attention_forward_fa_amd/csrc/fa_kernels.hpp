@@ -44,9 +44,12 @@ struct DecodeParams {
   const int* block_table;      // [B, bt_stride] or nullptr (dense)
   int bt_stride;
   int page_size;               // paged: tokens per page; dense: Smax
+  int64_t cache_rows;          // token rows in k (and v): pages * page_size, or B * Smax
   int log2_page;               // log2(page_size) when page_size is a power of two, else -1
   float* out_partial;          // [B, Sq, Hq, num_splits, D] fp32
   float* lse_partial;          // [B, Sq, Hq, num_splits] fp32
+  int2* order;                 // [B] schedule order: (b, cache_seqlens[b]) by decreasing split length;
+                               // nullptr: B <= 64, ranked inside the decode kernel
   int B, Sq, Hq, Hkv, group;
   int num_splits;
   float scale;

@@ -93,9 +93,11 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
                         const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
                         const int64_t* o_stride, const fa_attn_opts* opts, void* stream);
 
-/* Bytes of float32 workspace fa_fwd_kvcache needs: B*Sq*Hq*num_splits*(D+1)*4,
- * the out partials padded to 256 bytes, then the lse partials. num_splits as
- * passed to fa_fwd_kvcache after resolving 0 (see fa_kvcache_num_splits). */
+/* Bytes of workspace fa_fwd_kvcache needs: the float32 out partials
+ * [B, Sq, Hq, num_splits, D], the float32 lse partials [B, Sq, Hq, num_splits]
+ * and the int32 schedule order [B, 2], each padded to 256 bytes; about
+ * B*Sq*Hq*num_splits*(D+1)*4.  num_splits as passed to fa_fwd_kvcache after
+ * resolving 0 (see fa_kvcache_num_splits). */
 size_t fa_kvcache_workspace_size(int B, int Sq, int Hq, int D, int num_splits);
 
 /* The split count fa_fwd_kvcache uses when passed num_splits = 0, for a cache
@@ -117,7 +119,9 @@ int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits);
  *     queries are bottom-right aligned against them.
  *   num_splits: 1..64, or 0 for fa_kvcache_num_splits(); (Hq/Hkv)*Sq <= 16.
  *   workspace: device memory of at least fa_kvcache_workspace_size() bytes,
- *     256-byte aligned; it holds the per-split partials between the two kernels.
+ *     256-byte aligned, any contents; it holds the per-split partials between
+ *     the kernels.  Calls sharing a workspace must not overlap in time.
+ *   B*num_splits*Hkv <= 2^30.
  */
 fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
                          const int* cache_seqlens, const int* block_table, int block_table_stride,

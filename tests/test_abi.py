@@ -100,8 +100,9 @@ def test_varlen_rejects(lib):
 
 
 def test_kvcache_workspace_and_rejects(lib):
-    assert lib.fa_kvcache_workspace_size(64, 1, 32, 128, 16) == 64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
-    assert lib.fa_kvcache_workspace_size(1, 1, 1, 64, 3) == 768 + 256
+    # out partials, lse partials, schedule order (b, len) pairs; each padded to 256 bytes
+    assert lib.fa_kvcache_workspace_size(64, 1, 32, 128, 16) == 64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4 + 512
+    assert lib.fa_kvcache_workspace_size(1, 1, 1, 64, 3) == 768 + 256 + 256
     assert lib.fa_kvcache_num_splits(64, 8, 16384, 16) == 16
     assert 1 <= lib.fa_kvcache_num_splits(64, 8, 16384, 0) <= 64
     assert lib.fa_kvcache_num_splits(1, 1, 100, 0) == 1

@@ -225,6 +225,48 @@ def test_paged_decode_edge_cases(page, lens, ns, sq, fill, D, dt):
     assert torch.equal(out, b[0]) and torch.equal(lse, b[1])
 
 
+def test_paged_decode_many_sequences():
+    # more than 64 sequences: the schedule order comes from its own kernel
+    lens = [int(x) for x in np.random.default_rng(80).integers(0, 400, 80)]
+    lens[3] = 0
+    pc = inputs.paged_cache(80, 1, 8, 2, 64, torch.bfloat16, seed=80, page_size=32, lengths=lens, tail_fill="nan")
+    c = dict(q=pc.q, k_pool=pc.k_pool, v_pool=pc.v_pool, block_table=pc.block_table,
+             cache_seqlens=pc.cache_seqlens, page_size=32)
+    out, lse = run_paged(c, num_splits=3)
+    ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, 32)
+    check(out, lse, ro, rl, torch.bfloat16, "paged B=80")
+    kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
+    vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
+    b = run_paged(c, block_table=False, dense=(kd, vd), num_splits=3)
+    assert torch.equal(out, b[0]) and torch.equal(lse, b[1])
+
+
+def test_paged_decode_pool_beyond_4gib():
+    # the same pages placed past the first 4 GiB of a larger pool take the
+    # 64-bit addressing path; results must not change at all
+    lens = [700, 1, 300, 512]
+    page, Hkv, D = 256, 8, 128
+    pc = inputs.paged_cache(len(lens), 1, 32, Hkv, D, torch.bfloat16, seed=44, page_size=page, lengths=lens)
+    c = dict(q=pc.q, k_pool=pc.k_pool, v_pool=pc.v_pool, block_table=pc.block_table,
+             cache_seqlens=pc.cache_seqlens, page_size=page)
+    small = run_paged(c, num_splits=3)
+    n = pc.k_pool.shape[0]
+    page_bytes = page * Hkv * D * 2
+    first = (4 << 30) // page_bytes + 3                 # first page index past 4 GiB
+    big_k = torch.zeros((first + n, page, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    big_v = torch.zeros_like(big_k)
+    big_k[first:] = pc.k_pool.to(DEV)
+    big_v[first:] = pc.v_pool.to(DEV)
+    bt = pc.block_table.clone()
+    bt[bt >= 0] += first
+    out, lse = fa.fwd_kvcache(pc.q.to(DEV), big_k, big_v, pc.cache_seqlens.to(DEV), block_table=bt.to(DEV),
+                              num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), small[0]) and torch.equal(lse.cpu(), small[1])
+    del big_k, big_v
+    torch.cuda.empty_cache()
+
+
 def test_kvcache_options_match_oracle():
     pc = inputs.paged_cache(3, 1, 8, 8, 64, torch.float16, seed=9, page_size=64, lengths=[700, 64, 1000])
     slopes = inputs.alibi_slopes(8)
@@ -240,23 +282,39 @@ def test_kvcache_options_match_oracle():
         check(out, lse, ro, rl, torch.float16, f"kvcache {opts}")
 
 
-def test_combine_standalone():
-    rng = np.random.default_rng(3)
-    B, S, H, D, n = 2, 3, 4, 128, 6
+def _combine_case(seed, B, S, H, D, n, nan_rows=True):
+    rng = np.random.default_rng(seed)
     op = rng.standard_normal((B, S, H, D, n)).astype(np.float32)
     lp = (rng.standard_normal((B, S, H, n)) * 3).astype(np.float32)
-    lp[0, 0, 0, :] = -np.inf                   # a row with no keys anywhere
-    lp[1, 2, 3, [1, 4]] = -np.inf              # some empty splits
-    op[1, 2, 3, :, 1] = np.nan                 # whose partials must not be read
-    out, lse = fa.combine(torch.from_numpy(op).to(DEV), torch.from_numpy(lp).to(DEV), out_dtype=torch.float16)
-    torch.cuda.synchronize()
+    if nan_rows:
+        lp[0, 0, 0, :] = -np.inf               # a row with no keys anywhere
+        op[0, 0, 0] = np.nan
+        if n > 1:
+            lp[-1, -1, -1, ::2] = -np.inf      # some empty splits
+            op[-1, -1, -1, :, ::2] = np.nan    # whose partials must not be read
+    return op, lp
+
+
+@pytest.mark.parametrize("B,S,H,D,n", [(2, 3, 4, 128, 6), (2, 1, 3, 128, 1), (1, 2, 5, 64, 64), (3, 1, 2, 64, 3)])
+def test_combine_standalone(B, S, H, D, n):
+    op, lp = _combine_case(B * 100 + n, B, S, H, D, n)
+    lpd = torch.from_numpy(lp).to(DEV)
     ro, rl = ref.combine(np.nan_to_num(op), lp)
-    check(out.cpu(), lse.cpu(), ro, rl, torch.float16, "combine")
-    # the pages' [B,S,H,D,n] order and a transposed view give the same result
-    opt = torch.from_numpy(np.ascontiguousarray(op.transpose(0, 1, 2, 4, 3))).to(DEV).transpose(3, 4)
-    out2, lse2 = fa.combine(opt, torch.from_numpy(lp).to(DEV), out_dtype=torch.float16)
+    # the pages' [B,S,H,D,n] order (any-stride kernel) ...
+    out, lse = fa.combine(torch.from_numpy(op).to(DEV), lpd, out_dtype=torch.float16)
     torch.cuda.synchronize()
-    assert torch.equal(out.cpu(), out2.cpu()) and torch.equal(lse.cpu(), lse2.cpu())
+    check(out.cpu(), lse.cpu(), ro, rl, torch.float16, f"combine [B,S,H,D,n] n={n}")
+    # ... and a [B,S,H,n,D] buffer seen through a transposed view (the decode
+    # workspace order, row kernel): same result up to summation order
+    opt = torch.from_numpy(np.ascontiguousarray(op.transpose(0, 1, 2, 4, 3))).to(DEV).transpose(3, 4)
+    out2, lse2 = fa.combine(opt, lpd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check(out2.cpu(), lse2.cpu(), ro, rl, torch.bfloat16, f"combine [B,S,H,n,D] n={n}")
+    out3, _ = fa.combine(opt, lpd, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    d = (out3.cpu().float() - out.cpu().float()).abs()
+    ulp = torch.maximum(out.cpu().float().abs(), torch.tensor(6.1e-5)) * 2.0 ** -10
+    assert bool((d <= ulp + 1e-7).all()), f"row kernel vs any-stride kernel differ by {d.max().item()}"
 
 
 def test_empty_batch_is_noop():
