@@ -108,6 +108,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   constexpr int KROW = D + 8;             // K LDS row stride: conflict-free 16-byte reads
   constexpr int CH = D / 8;               // 16-byte pieces per K/V row
   constexpr int NL = C * CH / 64;         // K (and V) pieces a lane loads per chunk, one per row
+  constexpr int RPI = 64 / CH;            // rows covered by one 16-byte load of all 64 lanes
   constexpr int NE = MODE == 2 ? NL : 1;  // page numbers a lane holds per chunk
   static_assert(NL * 64 == C * CH, "");
   constexpr int NG = C / 16;              // 16-token groups per chunk (MFMA M blocks of S^T)
@@ -220,17 +221,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       } else {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-          const int r = (i * 64 + lane) / CH;
+          const int r = RPI * i + lane / CH;
           e[i] = bt[d.ok ? div_page(min(d.base + r, d.te - 1)) : 0];
         }
       }
     }
   };
-  // the chunk's K and V rows (rows past the item's end repeat its last row), the
-  // item's query rows (rows past the group read row 0) and ALiBi slopes (a
-  // stand-in address without slopes); qs and sls are raw loaded values
+  // LDS tile: row RPI*i + lane/CH, 16-byte piece lane%CH, from one base address
+  // per lane and constant offsets
+  T* const kst = kbuf + (lane / CH) * KROW + (lane % CH) * 8;
+  T* const vst = vbuf + (lane / CH) * VROW + (lane % CH) * 8;
+  auto put = [&](int i, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) __attribute__((always_inline)) {
+    *(u32x4*)(kst + i * RPI * KROW) = kr[i];
+    *(u32x4*)(vst + i * RPI * VROW) = vr[i];
+  };
+
+  // Load chunk d: its K and V rows (rows past the item's end repeat its last
+  // row), the item's query rows (rows past the group read row 0) and ALiBi
+  // slopes (a stand-in address without slopes); qs and sls are raw loaded
+  // values.  With Swap, the chunk the registers hold is stored to the LDS tile
+  // piece by piece, each register reloaded right after its store, so the new
+  // chunk's loads leave as soon as the old one starts to arrive.
   auto issue = [&](const DecodeChunk& d, const int (&e)[NE], u32x4 (&kr)[NL], u32x4 (&vr)[NL],
-                   u32x4 (&qs)[KSTEP], float& sls) __attribute__((always_inline)) {
+                   u32x4 (&qs)[KSTEP], float& sls, auto Swap) __attribute__((always_inline)) {
+    constexpr bool swap = decltype(Swap)::value;
     const int b = d.ok ? d.b : 0, hk = d.ok ? d.hk : 0;
     const T* kh = (const T*)p.k + (int64_t)hk * D;
     const T* vh = (const T*)p.v + (int64_t)hk * D;
@@ -245,7 +259,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       // per lane, shared by K and V.  Lane rows are t_i = base + RPI*i + lr; a
       // row's offset steps by RPI rows per load, plus the page jump past bnd;
       // rows past the item's end reread its last row.
-      constexpr int RPI = 64 / CH;          // rows per load instruction
       const char* kb8 = (const char*)p.k;
       const char* vb8 = (const char*)p.v;
       const uint32_t rowb = (uint32_t)(row_elems * sizeof(T));
@@ -259,6 +272,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
           int row = e[i] * page + (t - div_page(t) * page);
           if (!d.ok) row = 0;
           const uint32_t off = (uint32_t)row * rowb + lane_off;
+          if constexpr (swap) put(i, kr, vr);
           kr[i] = *(const u32x4*)(kb8 + off);
           vr[i] = *(const u32x4*)(vb8 + off);
         }
@@ -279,6 +293,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
           const int t = t0 + RPI * i;
           uint32_t off = off0 + (uint32_t)i * stepb + (t >= bnd ? jump : 0u);
           if (t > tl || !d.ok) off = d.ok ? off_last : lane_off;
+          if constexpr (swap) put(i, kr, vr);
           kr[i] = *(const u32x4*)(kb8 + off);
           vr[i] = *(const u32x4*)(vb8 + off);
         }
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     } else {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int slot = i * 64 + lane, r = slot / CH, c = slot - r * CH;
+        const int r = RPI * i + lane / CH, c = lane % CH;
         const int t = min(d.base + r, d.te - 1);
         int64_t row;
         if constexpr (MODE == 0) {
@@ -298,6 +313,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
           row = (int64_t)e[i] * page + (t - div_page(t) * page);
         }
         if (!d.ok) row = 0;
+        if constexpr (swap) put(i, kr, vr);
         kr[i] = *(const u32x4*)(kh + row * row_elems + c * 8);
         vr[i] = *(const u32x4*)(vh + row * row_elems + c * 8);
       }
@@ -308,15 +324,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     for (int ks = 0; ks < KSTEP; ++ks) qs[ks] = *(const u32x4*)(qrow + ks * 32);
     sls = *(p.alibi ? p.alibi + hq : p.lse_partial);
   };
-  auto store = [&](const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int slot = i * 64 + lane, r = slot / CH, c = slot - r * CH;
-      *(u32x4*)(&kbuf[r * KROW + c * 8]) = kr[i];
-      *(u32x4*)(&vbuf[r * VROW + c * 8]) = vr[i];
-    }
-  };
-
   // ---- per-item row state.  Row n sees tokens [rlo, rhi] of the item; every
   // live row sees [wlo, whi], so chunks inside it need no masking.
   V8 qb[KSTEP];
@@ -446,13 +453,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     }
   };
 
-  // ---- pipeline.  Step j: wait for chunk c_j and store it to the LDS tile;
-  // request the pages of c_{j+2}; issue the loads of c_{j+1} into the registers
-  // c_j has left; compute c_j from LDS while c_{j+1} is in flight.  One chunk
-  // in flight per wave, issued as one batch, reads HBM faster than a deeper
-  // trickle of loads.  Page numbers are requested before the loads of the
-  // chunk ahead of them, so waiting for them only waits for consumed chunks.
-  // The LDS tile is reused at once: a wave's LDS accesses complete in order.
+  // ---- pipeline.  Step j: request the pages of c_{j+2}; store chunk c_j to
+  // the LDS tile while loading c_{j+1} into the registers it leaves; compute c_j
+  // from LDS while c_{j+1} is in flight.  One chunk in flight per wave reads HBM
+  // faster than a deeper trickle of loads.  Page numbers are requested before
+  // the loads of the chunk ahead of them, so waiting for them only waits for
+  // consumed chunks.  The LDS tile is reused at once: a wave's LDS accesses
+  // complete in order.
   DecodeChunk dq[2], dc;      // chunks with pages requested (by j % 2) / the chunk in registers
   int ev[2][NE];
   u32x4 kr[NL], vr[NL];
@@ -464,17 +471,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   dq[1] = dq[0];
   advance(dq[1]);
   request(dq[1], ev[1]);                              // c1
-  issue(dq[0], ev[0], kr, vr, qs, sl);
+  issue(dq[0], ev[0], kr, vr, qs, sl, std::false_type{});
   dc = dq[0];
   // step j with s = j % 2: dq[s ^ 1] holds c_{j+1}
   auto step = [&](auto S) __attribute__((always_inline)) -> bool {
     constexpr int s0 = decltype(S)::value, s1 = s0 ^ 1;
-    store(kr, vr);                                    // c_j
     if (dc.first) begin_item(dc, qs, sl);
     dq[s0] = dq[s1];
     advance(dq[s0]);                                  // c_{j+2}
     request(dq[s0], ev[s0]);
-    issue(dq[s1], ev[s1], kr, vr, qs, sl);            // c_{j+1}
+    issue(dq[s1], ev[s1], kr, vr, qs, sl, std::true_type{});   // store c_j, load c_{j+1}
     compute(dc);
     dc = dq[s1];
     return dc.ok;
