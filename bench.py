@@ -48,9 +48,13 @@ def causal_pairs(Sq: int, Sk: int) -> int:
     return total
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(which: str = "prefill") -> str:
+    """Short hash of the sources a kernel is built from; stored traffic figures
+    are used only while it matches."""
+    files = {"prefill": ("prefill.hip", "fa_device.hpp", "fa_kernels.hpp"),
+             "decode": ("decode.hip", "combine.hip", "fa_device.hpp", "fa_kernels.hpp")}[which]
     h = hashlib.sha256()
-    for f in ("prefill.hip", "fa_device.hpp", "fa_kernels.hpp"):
+    for f in files:
         with open(os.path.join(ROOT, "exact_attention_forward_fa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -193,14 +197,18 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {n} bytes read + {n} bytes written")
 
-    traffic = None
+    # HBM bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE,
+    # scaled by a device copy), only while the kernel sources are unchanged
+    traffic = d_traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("prefill_source_sha") == kernel_source_hash():
+        if tr.get("prefill_source_sha") == kernel_source_hash("prefill"):
             traffic = tr["prefill_bytes_per_launch"]
+        if tr.get("decode_source_sha") == kernel_source_hash("decode"):
+            d_traffic = tr["decode_bytes_per_call"]
     except (OSError, ValueError, KeyError):
-        traffic = None
+        traffic = d_traffic = None
 
     line = {
         "metric": "attn fwd TFLOP/s (causal, B4 S4096 H32 D64 fp16) + paged decode HBM GB/s",
@@ -226,7 +234,7 @@ def main():
         "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms_mean": round(d_mean, 5),
                    "ms_min": round(min(d_ms), 5), "bytes": d_bytes, "dtype": "bf16",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}},
+                                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": d_traffic}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None if cpu is None else {kk: cpu[kk] for kk in ("value", "unit", "cores", "kind", "sample")},

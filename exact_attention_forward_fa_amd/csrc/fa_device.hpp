@@ -70,6 +70,11 @@ struct BF16 {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0): every vector-memory access issued so far has completed.
+// Placed before a loop, it tells the compiler that registers loaded before the
+// loop are ready, so waits inside the loop count only the loop's own loads.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Value of x held by the lane in the other 32-lane half (lane l <-> l ^ 32).
 __device__ __forceinline__ float other_half(float x) {
   u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -18,8 +18,9 @@
 //    score layout already is the B layout up to a fixed permutation of the
 //    contraction index, applied identically to V); V^T comes out of LDS with the
 //    transposing read ds_read_b64_tr_b16.
-//  * K and V tiles are double-buffered in LDS with XOR-swizzled 16-byte chunks;
-//    the next tile's global loads are issued before the current tile's math.
+//  * K and V tiles are double-buffered in LDS with padded rows (conflict-free
+//    reads, see k_stride / v_stride); the next tile's global loads are issued
+//    before the current tile's math.
 //  * scale·log2(e) is folded into the exp2 argument (one FMA + v_exp_f32 per score).
 //  * tiles that are fully masked for a wave are skipped; mask arithmetic runs only
 //    on tiles that straddle a mask edge.
@@ -319,6 +320,7 @@ void prefill_kernel(PrefillParams p) {
     gload(t_lo);
     swrite(0);
   }
+  wait_vmem_all();   // Q operands ready: the loop waits only for its own tile loads
   __syncthreads();
 
   for (int t = t_lo; t < t_hi; ++t) {
@@ -491,6 +493,7 @@ void prefill_pp_kernel(PrefillParams p) {
 
   if (n_t > 0) { gload(0); swrite(0); }
   if (n_t > 1) { gload(1); swrite(1); }
+  wait_vmem_all();   // Q operands ready: the loop waits only for its own tile loads
   if (n_t > 2) gload(2);
   barrier();
   if (grp == 1) barrier();                 // group 1 runs one phase behind
