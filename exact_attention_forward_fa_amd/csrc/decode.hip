@@ -367,7 +367,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       for (int ks = 0; ks < KSTEP; ++ks)
         s[g] = E::mfma16(*(const V8*)(kb_ + 16 * g * KROW + ks * 32), qb[ks], s[g]);
     }
-    // scores of tokens base + 16g + 4q4 + r for row n, in log2 units
+    // scores of tokens base + 16g + 4q4 + r for row n; times mult they are in
+    // log2 units (plain scores keep the scale folded into the exp argument)
+    const bool plain = !(p.softcap > 0.f) && !p.alibi;
+    const float mult = plain ? sl2 : 1.f;
     if (p.softcap > 0.f) {
 #pragma unroll
       for (int g = 0; g < NG; ++g)
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
           const float e = exp2_fast(s[g][r] * cap_in);
           s[g][r] = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
         }
-    } else {
+    } else if (p.alibi) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) s[g] *= sl2;
     }
@@ -398,8 +401,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     float mx = kNegInf;
 #pragma unroll
     for (int g = 0; g < NG; ++g) mx = fmaxf(mx, fmaxf(fmaxf(s[g][0], s[g][1]), fmaxf(s[g][2], s[g][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_halves(max_xor16(mx)) * mult;           // the row's four lanes: l, l^16, l^32, l^48
     const float m_new = fmaxf(m, mx);
     if (__any(m_new > m + kTauD)) {
       const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
@@ -419,7 +421,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
-          const float p0 = exp2_fast(s[2 * hh + g][r] - m_use), p1 = exp2_fast(s[2 * hh + g][r + 1] - m_use);
+          const float p0 = exp2_fast(fmaf(s[2 * hh + g][r], mult, -m_use));
+          const float p1 = exp2_fast(fmaf(s[2 * hh + g][r + 1], mult, -m_use));
           const V2 pp = E::pack(p0, p1);
           bop[4 * g + r] = pp[0];
           bop[4 * g + r + 1] = pp[1];
@@ -438,10 +441,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     }
     if (d.last) {
       // the four lanes of a row hold partial sums over their own tokens
-      float lt = l + __shfl_xor(l, 16, 64);
-      lt += __shfl_xor(lt, 32, 64);
-      float lxt = lx + __shfl_xor(lx, 16, 64);
-      lxt += __shfl_xor(lxt, 32, 64);
+      const float lt = sum_halves(sum_xor16(l));
+      const float lxt = sum_halves(sum_xor16(lx));
       if (live) {
         const int64_t prow = prow_of(d);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;

@@ -120,7 +120,8 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   if ((st = check_strides("q", qs, 3)) || (st = check_strides("k", ks, 3)) || (st = check_strides("v", vs, 3)) ||
       (st = check_strides("out", os, 3)))
     return st;
-  const int64_t nqt = (Sq + fa::kPrefillBlockM - 1) / fa::kPrefillBlockM;
+  const int bm = fa::prefill_block_m(D);
+  const int64_t nqt = (Sq + bm - 1) / bm;
   if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
   fa::PrefillParams p{};
@@ -164,7 +165,8 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   if ((st = check_strides("q", qs, 2)) || (st = check_strides("k", ks, 2)) || (st = check_strides("v", vs, 2)) ||
       (st = check_strides("out", os, 2)))
     return st;
-  const int64_t nqt = (max_seqlen_q + fa::kPrefillBlockM - 1) / fa::kPrefillBlockM;
+  const int bm = fa::prefill_block_m(D);
+  const int64_t nqt = (max_seqlen_q + bm - 1) / bm;
   if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
   fa::PrefillParams p{};

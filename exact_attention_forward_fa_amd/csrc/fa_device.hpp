@@ -92,6 +92,17 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max / sum of x over the pair of lanes {l, l ^ 16} (v_permlane16_swap: the two
+// results hold the lane's own value and its partner's, in some order)
+__device__ __forceinline__ float max_xor16(float x) {
+  u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element (i % 4) of the 8-byte chunk addressed by lane
 // 4*j + i/4, for j = 0..3.

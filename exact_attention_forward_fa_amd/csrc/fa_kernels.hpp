@@ -89,6 +89,7 @@ hipError_t launch_combine(Dtype dt, const CombineParams& p, hipStream_t s);
 #ifndef FA_PREFILL_RB128
 #define FA_PREFILL_RB128 1
 #endif
-constexpr int kPrefillBlockM = 256;   // query rows per prefill workgroup (NW * 32 * RB)
+// query rows per prefill workgroup for head dim D (the host sizes the grid with it)
+int prefill_block_m(int D);
 
 }  // namespace fa

@@ -50,7 +50,10 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 //  * V rows of 2D+64 bytes: a transposing read covers 4 rows x 64 bytes per 32
 //    lanes, and the 64-byte row offsets map those rows to 4 disjoint bank ranges.
 template <int D> constexpr int k_stride() { return D + 8; }
-template <int D> constexpr int v_stride() { return D + 32; }
+#ifndef FA_PREFILL_VPAD
+#define FA_PREFILL_VPAD 32
+#endif
+template <int D> constexpr int v_stride() { return D + FA_PREFILL_VPAD; }
 
 template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_PREFILL_WAVES_PER_EU)))
@@ -79,9 +82,15 @@ void prefill_kernel(PrefillParams p) {
   // 8 XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
   // within a head the longest (last) query tiles go first.
   int id = blockIdx.x;
+#ifndef FA_PREFILL_NO_REMAP
   if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
+#endif
   const int head = id / p.n_qtiles;
+#ifdef FA_PREFILL_LIGHT_FIRST
+  const int qt = id - head * p.n_qtiles;
+#else
   const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);
+#endif
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
 
@@ -638,10 +647,14 @@ template <int D> struct Shape;
 template <> struct Shape<64> { static constexpr int NW = FA_PREFILL_NW64, RB = FA_PREFILL_RB64, BN = 64; };
 template <> struct Shape<128> { static constexpr int NW = FA_PREFILL_NW128, RB = FA_PREFILL_RB128, BN = 64; };
 
+int prefill_block_m(int D) {
+  if (D >= FA_PREFILL_PINGPONG_MIN_D) return 8 * 32;
+  return D == 64 ? Shape<64>::NW * 32 * Shape<64>::RB : Shape<128>::NW * 32 * Shape<128>::RB;
+}
+
 template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
   using S = Shape<D>;
-  static_assert(S::NW * 32 * S::RB == kPrefillBlockM, "workgroup row count must match the host grid");
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
   if (D >= FA_PREFILL_PINGPONG_MIN_D)
     hipLaunchKernelGGL((prefill_pp_kernel<E, D, 64, SC, AL>), dim3(grid), dim3(512), 0, s, p);
