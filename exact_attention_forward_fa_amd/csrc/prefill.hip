@@ -82,15 +82,9 @@ void prefill_kernel(PrefillParams p) {
   // 8 XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
   // within a head the longest (last) query tiles go first.
   int id = blockIdx.x;
-#ifndef FA_PREFILL_NO_REMAP
   if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
-#endif
   const int head = id / p.n_qtiles;
-#ifdef FA_PREFILL_LIGHT_FIRST
-  const int qt = id - head * p.n_qtiles;
-#else
   const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);
-#endif
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
 
