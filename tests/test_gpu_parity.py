@@ -156,6 +156,9 @@ EDGE = [
     (3, 1, 333, 8, 2, 128, torch.float16, dict(causal=True)),            # decode shape via prefill
     (1, 64, 1, 2, 2, 64, torch.float16, dict(causal=True)),              # Sk = 1
     (1, 33, 33, 2, 2, 64, torch.float16, dict(softmax_scale=0.3)),
+    (2, 300, 300, 4, 4, 128, torch.float16, dict()),                     # plain D=128 fp16, non-causal
+    (1, 260, 200, 4, 2, 64, torch.bfloat16, dict(alibi=True, window=(50, 20))),
+    (1, 220, 150, 4, 1, 64, torch.float16, dict(alibi=True, softcap=10.0, causal=True)),
 ]
 
 
@@ -222,6 +225,49 @@ def test_paged_decode_edge_cases(page, lens, ns, sq, fill, D, dt):
     kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
     vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
     b = run_paged(c, block_table=False, dense=(kd, vd), num_splits=ns, causal=True)
+    assert torch.equal(out, b[0]) and torch.equal(lse, b[1])
+
+
+def test_varlen_options_d128():
+    lq, lk = [40, 1, 300, 97], [60, 50, 300, 128]
+    q, k, v, cq, ck = inputs.varlen_pack(lq, lk, 8, 2, 128, torch.bfloat16, seed=73)
+    qd, kd, vd, cqd, ckd = gpu(q, k, v, cq, ck)
+    slopes = inputs.alibi_slopes(8)
+    for opts in (dict(causal=True, softcap=15.0), dict(alibi=True, window=(30, 0), causal=True), dict(softcap=5.0, alibi=True)):
+        gopts = dict(causal=opts.get("causal", False), window_size=opts.get("window", (-1, -1)),
+                     softcap=opts.get("softcap", 0.0), alibi_slopes=slopes.to(DEV) if opts.get("alibi") else None)
+        out, lse = fa.fwd_varlen(qd, kd, vd, cqd, ckd, max(lq), max(lk), **gopts)
+        torch.cuda.synchronize()
+        ro, rl = ref.attention_varlen(q, k, v, cq, ck, causal=opts.get("causal", False), window=opts.get("window", (-1, -1)),
+                                      softcap=opts.get("softcap", 0.0), alibi_slopes=slopes if opts.get("alibi") else None)
+        check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"varlen D128 {opts}")
+
+
+@pytest.mark.parametrize("page,Hq,Hkv,sq,D,dt,ns,opts", [
+    (100, 8, 2, 1, 128, torch.bfloat16, 3, dict()),                                   # pages >= 64, not a power of two
+    (64, 32, 4, 2, 128, torch.bfloat16, 4, dict(causal=True)),                        # 16 query rows per kv head
+    (128, 8, 2, 2, 128, torch.bfloat16, 5, dict(causal=True, window=(90, 0), softcap=30.0, alibi=True)),
+    (16, 8, 4, 3, 64, torch.float16, 2, dict(causal=True, window=(20, 0), alibi=True)),
+    (256, 8, 2, 1, 128, torch.bfloat16, 1, dict(softcap=7.0)),                        # one split
+])
+def test_paged_decode_options(page, Hq, Hkv, sq, D, dt, ns, opts):
+    print("paged options", page, Hq, Hkv, sq, D, dt, ns, opts, flush=True)
+    lens = [300, 1, 777, 64, 129]
+    pc = inputs.paged_cache(len(lens), sq, Hq, Hkv, D, dt, seed=page + 7 * sq, page_size=page, lengths=lens,
+                            tail_fill="nan")
+    slopes = inputs.alibi_slopes(Hq) if opts.get("alibi") else None
+    c = dict(q=pc.q, k_pool=pc.k_pool, v_pool=pc.v_pool, block_table=pc.block_table,
+             cache_seqlens=pc.cache_seqlens, page_size=page)
+    gkw = dict(causal=opts.get("causal", False), window_size=opts.get("window", (-1, -1)),
+               softcap=opts.get("softcap", 0.0), alibi_slopes=None if slopes is None else slopes.to(DEV))
+    out, lse = run_paged(c, num_splits=ns, **gkw)
+    ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, page,
+                                   causal=opts.get("causal", False), window=opts.get("window", (-1, -1)),
+                                   softcap=opts.get("softcap", 0.0), alibi_slopes=slopes)
+    check(out, lse, ro, rl, dt, f"paged options p{page} sq{sq} {opts}")
+    kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
+    vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
+    b = run_paged(c, block_table=False, dense=(kd, vd), num_splits=ns, **gkw)
     assert torch.equal(out, b[0]) and torch.equal(lse, b[1])
 
 
