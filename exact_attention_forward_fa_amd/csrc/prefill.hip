@@ -30,6 +30,7 @@
 namespace fa {
 
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
+constexpr float kTauPow = 256.f;   // 2^kTau
 
 // Head dims from which the ping-pong kernel is used.  With D = 64 the softmax
 // phase outweighs the MFMA phase and a single wave per SIMD cannot issue VALU
@@ -56,7 +57,7 @@ template <int D> constexpr int k_stride() { return D + 8; }
 template <int D> constexpr int v_stride() { return D + FA_PREFILL_VPAD; }
 
 template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_PREFILL_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -162,15 +163,35 @@ void prefill_kernel(PrefillParams p) {
 
   // ---- global -> register staging of one K/V tile (rows past sk are clamped to a
   // real row; their scores are masked, so their values only ever meet p = 0)
+  // Whole tiles are addressed as a scalar tile base plus a fixed 32-bit byte offset
+  // per lane; the last, partial tile clamps row by row.
   u32x4 kst[LOADS], vst[LOADS];
-  auto gload = [&](int tile) {
-    const int j0 = tile * BN;
+  uint32_t koff[LOADS], voff[LOADS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
-      const int j = min(j0 + r, sk - 1);
-      kst[i] = *(const u32x4*)(kp + (int64_t)j * p.k_ss + c * 8);
-      vst[i] = *(const u32x4*)(vp + (int64_t)j * p.v_ss + c * 8);
+  for (int i = 0; i < LOADS; ++i) {
+    const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+    koff[i] = (uint32_t)(r * p.k_ss + c * 8) * (uint32_t)sizeof(T);
+    voff[i] = (uint32_t)(r * p.v_ss + c * 8) * (uint32_t)sizeof(T);
+  }
+  const bool off32 = p.k_ss >= 0 && p.v_ss >= 0 && p.k_ss < (1 << 24) / BN && p.v_ss < (1 << 24) / BN;
+  auto gload = [&](int tile) __attribute__((always_inline)) {
+    const int j0 = tile * BN;
+    if (off32 && j0 + BN <= sk) {
+      const char* kt = (const char*)(kp + (int64_t)j0 * p.k_ss);
+      const char* vt = (const char*)(vp + (int64_t)j0 * p.v_ss);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        kst[i] = *(const u32x4*)(kt + koff[i]);
+        vst[i] = *(const u32x4*)(vt + voff[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+        const int j = min(j0 + r, sk - 1);
+        kst[i] = *(const u32x4*)(kp + (int64_t)j * p.k_ss + c * 8);
+        vst[i] = *(const u32x4*)(vp + (int64_t)j * p.v_ss + c * 8);
+      }
     }
   };
   auto swrite = [&](int buf) {
@@ -187,8 +208,8 @@ void prefill_kernel(PrefillParams p) {
   // half is added at the end): l of the rounded P that feeds the P V product
   // (normalises out, so out is an exact convex combination of the rounded
   // weights) and lx of the unrounded fp32 P (gives an lse free of P rounding).
-  // The max is lazy: O, l, lx are rescaled only when some row's max grows by
-  // more than kTau (P then stays below 2^kTau), which leaves the result exact.
+  // m is lazy (see step): O, l, lx are rescaled only when m moves, which leaves
+  // the result exact.
   float m[RB], l[RB], lx[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -197,13 +218,10 @@ void prefill_kernel(PrefillParams p) {
     m[rb] = kNegInf; l[rb] = 0.f; lx[rb] = 0.f;
   }
 
-  // One tile for the wave's RB row blocks.  Mask arithmetic runs only when the
-  // tile straddles a mask edge for this wave (a uniform branch); a single body
-  // keeps register pressure at one copy of the tile state.
-  auto step = [&](bool edge, int j0, const T* Ks, const T* Vs) {
-    // S^T = K Q^T: s[rb][kb][r] is key j0 + 32kb + 8(r/4) + 4hi + (r%4) of row qrow[rb];
-    // each K operand read from LDS feeds the RB row blocks
-    f32x16 s[RB][KB];
+  // S^T = K Q^T for one tile: s[rb][kb][r] is key j0 + 32kb + 8(r/4) + 4hi + (r%4) of
+  // row qrow[rb]; each K operand read from LDS feeds the RB row blocks.  Softcap and
+  // ALiBi turn the scores into log2 units; masked scores become -inf when edge is set.
+  auto scores = [&](bool edge, int j0, const T* Ks, f32x16 (&s)[RB][KB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -217,9 +235,6 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[rb][kb] = E::mfma32(a, qr[rb][dc], s[rb][kb]);
       }
-
-    bool grow = false;
-    float m_new[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       if constexpr (!PLAIN) {
@@ -252,45 +267,93 @@ void prefill_kernel(PrefillParams p) {
             if (j < j_lo[rb] || j > j_hi[rb]) s[rb][kb][r] = kNegInf;
           }
       }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[rb][kb][r], s[rb][kb][r + 1]));
-      mx = max_halves(mx) * mult;
-      m_new[rb] = fmaxf(m[rb], mx);
-      grow |= m_new[rb] > m[rb] + kTau;
     }
-    if (__any(grow)) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float alpha = m_new[rb] == kNegInf ? 1.f : exp2_fast(m[rb] - m_new[rb]);
-        m[rb] = m_new[rb];
-        l[rb] *= alpha;
-        lx[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
-      }
-    }
+  };
 
-    // P = exp2(s - m), rounded for the P V product
-    V2 pk[RB][KB][8];
+  // P = exp2(s * mult - mu), rounded for the P V product, and this lane's sums of
+  // the rounded (ls) and unrounded (lxs) P of each row block
+  auto probs = [&](f32x16 (&s)[RB][KB], const float (&mu)[RB], V2 (&pk)[RB][KB][8], float (&ls)[RB],
+                   float (&lxs)[RB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float m_use = m[rb] == kNegInf ? 0.f : m[rb];
-      float ls = 0.f, lxs = 0.f;
+      float a = 0.f, ax = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_fast(fmaf(s[rb][kb][r], mult, -m_use));
-          const float p1 = exp2_fast(fmaf(s[rb][kb][r + 1], mult, -m_use));
+          const float p0 = exp2_fast(fmaf(s[rb][kb][r], mult, -mu[rb]));
+          const float p1 = exp2_fast(fmaf(s[rb][kb][r + 1], mult, -mu[rb]));
           pk[rb][kb][r >> 1] = E::pack(p0, p1);
-          ls = E::sum2(pk[rb][kb][r >> 1], ls);
-          lxs += p0 + p1;
+          a = E::sum2(pk[rb][kb][r >> 1], a);
+          ax += p0 + p1;
         }
-      l[rb] += ls;
-      lx[rb] += lxs;
+      ls[rb] = a;
+      lxs[rb] = ax;
+    }
+  };
+
+  // One tile for the wave's RB row blocks; mask arithmetic runs only when edge is set.
+  // The row max is not taken on every tile: once every row of the wave has a running
+  // max m, P is formed against it and kept when no lane's partial sum of P exceeds
+  // 2^kTau (then no single P does, and the rounded P stays far from overflow).
+  // Otherwise (first tile of a row, or a score more than about kTau above m) the
+  // tile is redone: the scores are recomputed, m moves to the exact new max, and O,
+  // l, lx are rescaled.  Any m not below the true max gives the same exact result.
+  auto step = [&](bool edge, int j0, const T* Ks, const T* Vs) __attribute__((always_inline)) {
+    f32x16 s[RB][KB];
+    V2 pk[RB][KB][8];
+    float ls[RB], lxs[RB];
+    bool unset = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) unset |= m[rb] == kNegInf;
+    bool redo = true;
+    if (!__any(unset)) {
+      scores(edge, j0, Ks, s);
+      probs(s, m, pk, ls, lxs);
+      bool big = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) big |= lxs[rb] > kTauPow;
+      redo = __any(big);
+    }
+    if (redo) {
+      scores(edge, j0, Ks, s);
+      float mu[RB];
+      bool grow = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          mx0 = fmaxf(fmaxf(mx0, s[rb][0][r]), s[rb][0][r + 1]);
+          mx1 = fmaxf(fmaxf(mx1, s[rb][KB - 1][r]), s[rb][KB - 1][r + 1]);
+        }
+#pragma unroll
+        for (int kb = 1; kb + 1 < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) mx0 = fmaxf(fmaxf(mx0, s[rb][kb][r]), s[rb][kb][r + 1]);
+        const float mx = max_halves(fmaxf(mx0, mx1)) * mult;
+        mu[rb] = fmaxf(m[rb], mx);
+        grow |= mu[rb] > m[rb];
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float alpha = mu[rb] == kNegInf ? 1.f : exp2_fast(m[rb] - mu[rb]);
+          m[rb] = mu[rb];
+          l[rb] *= alpha;
+          lx[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) mu[rb] = m[rb] == kNegInf ? 0.f : m[rb];
+      probs(s, mu, pk, ls, lxs);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l[rb] += ls[rb];
+      lx[rb] += lxs[rb];
     }
 
     // O^T += V^T P^T over 16-key chunks; each V operand read feeds the RB blocks.
@@ -319,17 +382,50 @@ void prefill_kernel(PrefillParams p) {
     }
   };
 
-  if (t_lo < t_hi) {
-    gload(t_lo);
+  // ---- tile order: first the tiles whose every key is seen by every row of the
+  // workgroup (tf_lo .. tf_hi-1; no mask arithmetic, no per-tile liveness test,
+  // and no branch between the two products), then the tiles at the mask edges
+  // (t_lo .. tf_lo-1, then tf_hi .. t_hi-1).  The online softmax is exact in
+  // any tile order.
+  int tf_lo = t_lo, tf_hi = t_lo;
+  {
+    int f_lo = 0, f_hi = sk - 1;   // keys seen by every row of the workgroup
+    if (p.wl >= 0) f_lo = max(0, ip_last - p.wl);
+    if (p.causal) f_hi = min(f_hi, ip_first);
+    if (p.wr >= 0) f_hi = min(f_hi, ip_first + p.wr);
+    if (f_lo <= f_hi) {
+      const int a = (f_lo + BN - 1) / BN, z = (f_hi + 1) / BN;
+      if (a < z) { tf_lo = a; tf_hi = z; }
+    }
+  }
+  const int n_full = tf_hi - tf_lo, n_front = tf_lo - t_lo, n_all = t_hi - t_lo;
+  auto tile_at = [&](int i) __attribute__((always_inline)) {
+    const int e = i - n_full;
+    return i < n_full ? tf_lo + i : (e < n_front ? t_lo + e : tf_hi + e - n_front);
+  };
+  bool wave_live = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) wave_live |= m0 + rb * NW * 32 + wave * 32 < sq;
+
+  if (n_all > 0) {
+    gload(tile_at(0));
     swrite(0);
   }
   wait_vmem_all();   // Q operands ready: the loop waits only for its own tile loads
   __syncthreads();
 
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    if (t + 1 < t_hi) gload(t + 1);
-    const int j0 = t * BN;
+  int i = 0;
+  for (; i < n_full; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < n_all) gload(tile_at(i + 1));
+    if (wave_live) step(false, (tf_lo + i) * BN, ksm[buf], vsm[buf]);
+    if (i + 1 < n_all) swrite(buf ^ 1);
+    __syncthreads();
+  }
+  for (; i < n_all; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < n_all) gload(tile_at(i + 1));
+    const int j0 = tile_at(i) * BN;
     bool any_live = false, all_full = true;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -340,7 +436,7 @@ void prefill_kernel(PrefillParams p) {
     if (any_live) {
       step(!all_full, j0, ksm[buf], vsm[buf]);
     }
-    if (t + 1 < t_hi) swrite(buf ^ 1);
+    if (i + 1 < n_all) swrite(buf ^ 1);
     __syncthreads();
   }
 
