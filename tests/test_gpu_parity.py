@@ -367,3 +367,50 @@ def test_empty_batch_is_noop():
     q = torch.empty(0, 16, 2, 64, dtype=torch.float16, device=DEV)
     out, lse = fa.fwd(q, q, q)
     assert out.shape == q.shape and lse.shape == (0, 2, 16)
+
+
+# ------------------------------------------------- running-max stress (rescale paths)
+
+def _ramped_qkv(B, Sq, Sk, H, D, dt, seed, profile):
+    """q with a common direction u and keys whose component along u follows a
+    profile over the key index, so the row max moves by several units (log2)
+    per 64-key tile: "rise" climbs steadily, "jump" has one block of keys far
+    above the rest, "fall" puts the largest scores first."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.ones(D, dtype=torch.float64) / D ** 0.5
+    q = torch.randn(B, Sq, H, D, generator=g, dtype=torch.float64) + 3.0 * u
+    j = torch.arange(Sk, dtype=torch.float64)
+    if profile == "rise":
+        a = 0.3 * j
+    elif profile == "jump":
+        a = torch.where((j >= Sk // 2) & (j < Sk // 2 + 40), torch.full_like(j, 60.0), torch.zeros_like(j))
+    else:
+        a = 0.3 * (Sk - 1 - j)
+    k = torch.randn(B, Sk, H, D, generator=g, dtype=torch.float64) * 0.5 + a[None, :, None, None] * u
+    v = torch.randn(B, Sk, H, D, generator=g, dtype=torch.float64)
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+@pytest.mark.parametrize("profile", ["rise", "jump", "fall"])
+@pytest.mark.parametrize("D,dt,causal", [(64, torch.float16, False), (64, torch.bfloat16, True),
+                                         (128, torch.float16, True), (128, torch.bfloat16, False)])
+def test_prefill_running_max_stress(profile, D, dt, causal):
+    print("case", profile, D, dt, causal, flush=True)
+    q, k, v = _ramped_qkv(1, 300, 700, 2, D, dt, 77 + D, profile)
+    out, lse = fa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention(q, k, v, causal=causal)
+    check(out.cpu(), lse.cpu(), ro, rl, dt, f"prefill {profile} D{D} {dt} causal={causal}")
+
+
+@pytest.mark.parametrize("profile", ["rise", "jump", "fall"])
+def test_decode_running_max_stress(profile):
+    print("case decode", profile, flush=True)
+    B, Smax, Hkv, Hq, D = 2, 1500, 2, 4, 128
+    q, k, v = _ramped_qkv(B, 1, Smax, Hkv, D, torch.bfloat16, 91, profile)
+    q = q.repeat_interleave(Hq // Hkv, dim=2).contiguous()
+    lens = torch.tensor([1500, 1100], dtype=torch.int32)
+    out, lse = fa.fwd_kvcache(q.to(DEV), k.to(DEV), v.to(DEV), lens.to(DEV), num_splits=3)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention_kvcache(q, k, v, lens)
+    check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"decode {profile}")
