@@ -198,6 +198,45 @@ def gather_pages(pool, block_table_row, n_tokens: int, page_size: int) -> np.nda
     return out
 
 
+def kvcache_append(k_cache, v_cache, k_new, v_new, cache_seqlens, block_table=None, page_size=None):
+    """Caches after writing new tokens ("FlashAttention 常用接口简单介绍", §3.3: k and v,
+    the optional new keys and values that update the cache).
+
+    Reading: cache_seqlens counts the tokens already cached, so token t of
+    sequence b's new block goes to cache position cache_seqlens[b] + t; with a
+    block table that position lives in page block_table[b, pos // page_size], row
+    pos % page_size (update notes, v2.5).  k_new/v_new: [B, S_new, Hkv, D].
+    A position outside the cache (past Smax, past the block-table row, or a page
+    number outside the pool) is not written: the library documents the same.
+    Returns float64 copies; the inputs are not modified.
+    """
+    kc = _f64(k_cache).copy()
+    vc = _f64(v_cache).copy()
+    kn = _f64(k_new)
+    vn = _f64(v_new)
+    lens = [int(x) for x in np.asarray(cache_seqlens).reshape(-1)]
+    for b in range(kn.shape[0]):
+        for t in range(kn.shape[1]):
+            pos = lens[b] + t
+            if pos < 0:
+                continue
+            if block_table is None:
+                if pos >= kc.shape[1]:
+                    continue
+                kc[b, pos] = kn[b, t]
+                vc[b, pos] = vn[b, t]
+            else:
+                row = np.asarray(block_table)[b]
+                if pos // page_size >= row.shape[0]:
+                    continue
+                page = int(row[pos // page_size])
+                if page < 0 or page >= kc.shape[0]:
+                    continue
+                kc[page, pos % page_size] = kn[b, t]
+                vc[page, pos % page_size] = vn[b, t]
+    return kc, vc
+
+
 def attention_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, page_size=None,
                       heads=None, **opts):
     """Attention of new queries against a KV cache ("FlashAttention 常用接口简单介绍", §3.3).

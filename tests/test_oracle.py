@@ -314,6 +314,61 @@ def test_paged_gather_equals_dense_cache():
         assert np.array_equal(a[0][bb], o[0]) and np.array_equal(a[1][bb], l[0])
 
 
+def _append_pins_hold(append):
+    """Pins of a cache-append function: (1) gathering the appended cache gives the
+    old prefix followed by the new tokens, (2) every other cache row is left as
+    it was, (3) attention against the appended cache equals plain attention over
+    the concatenated keys and values."""
+    from exact_attention_forward_fa_amd import inputs
+    final = [11, 5, 8]
+    S = 3
+    pc = inputs.paged_cache(3, 2, 4, 2, 8, torch.float16, seed=21, page_size=4, lengths=final, max_pages=4)
+    lens = pc.cache_seqlens - S                      # tokens cached before the append
+    g = torch.Generator().manual_seed(22)
+    kn = torch.randn(3, S, 2, 8, generator=g).to(torch.float16)
+    vn = torch.randn(3, S, 2, 8, generator=g).to(torch.float16)
+    kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
+    vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
+    ok = True
+    for paged in (True, False):
+        kc, vc = (pc.k_pool, pc.v_pool) if paged else (kd, vd)
+        bt, page = (pc.block_table, 4) if paged else (None, None)
+        k2, v2 = append(kc, vc, kn, vn, lens, bt, page)
+        touched = np.zeros(k2.shape[:2], dtype=bool)
+        for b, n in enumerate(final):
+            n0 = n - S
+            if paged:
+                got = ref.gather_pages(k2, pc.block_table[b], n, 4)
+                for t in range(n0, n):
+                    touched[int(pc.block_table[b, t // 4]), t % 4] = True
+            else:
+                got = k2[b, :n]
+                touched[b, n0:n] = True
+            want = np.concatenate([np.asarray(kc[b, :n0].float()) if not paged
+                                   else ref.gather_pages(kc, pc.block_table[b], n0, 4),
+                                   kn[b].double().numpy()])
+            ok &= np.array_equal(got, want)
+        ok &= np.array_equal(k2[~touched], np.asarray(kc.double())[~touched])
+        ok &= np.array_equal(v2[~touched], np.asarray(vc.double())[~touched])
+        o, l = ref.attention_kvcache(pc.q, k2, v2, pc.cache_seqlens, bt, page, causal=True)
+        for b, n in enumerate(final):
+            n0 = n - S
+            kk = np.concatenate([np.asarray(kd[b, :n0].double()), kn[b].double().numpy()])[None]
+            vv = np.concatenate([np.asarray(vd[b, :n0].double()), vn[b].double().numpy()])[None]
+            oo, ll = ref.attention(pc.q[b:b + 1], kk, vv, causal=True)
+            ok &= np.array_equal(o[b], oo[0]) and np.array_equal(l[b], ll[0])
+    return ok
+
+
+def test_kvcache_append_pins_and_planted_offsets():
+    assert _append_pins_hold(ref.kvcache_append)
+    # planted mistakes: new tokens one position late, or one early
+    late = lambda kc, vc, kn, vn, lens, bt, page: ref.kvcache_append(kc, vc, kn, vn, lens + 1, bt, page)
+    early = lambda kc, vc, kn, vn, lens, bt, page: ref.kvcache_append(kc, vc, kn, vn, lens - 1, bt, page)
+    assert not _append_pins_hold(late)
+    assert not _append_pins_hold(early)
+
+
 def test_combine_of_key_chunks_equals_whole():
     rng = np.random.default_rng(14)
     B, S, H, D, Sk = 2, 3, 2, 5, 23
