@@ -67,6 +67,9 @@ def load_library():
     lib.fa_kvcache_num_splits.restype = I
     lib.fa_fwd_kvcache.argtypes = [I, P, P, P, P, P, I, I, I, I, P, Z, P, P, I, I, I, I, I, OP, P]
     lib.fa_fwd_kvcache.restype = I
+    lib.fa_fwd_kvcache_append.argtypes = [I, P, P, P, P, P, I, I, I, I, P, P, I, I64P, I64P, P, Z, P, P,
+                                          I, I, I, I, I, OP, P]
+    lib.fa_fwd_kvcache_append.restype = I
     lib.fa_combine.argtypes = [P, P, I, I, I, I, I, I64P, I64P, I, P, I64P, P, P]
     lib.fa_combine.restype = I
     lib.fa_status_string.argtypes = [I]
@@ -212,12 +215,17 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits
 
     Split-KV over ``num_splits`` chunks (0 = library heuristic) followed by the
     LSE combine.  Returns (out [B,Sq,Hq,D], softmax_lse [B,Hq,Sq]).
+
+    With ``k`` and ``v`` ([B,S_new,Hkv,D]) the new tokens are first written into
+    the caches in place at positions cache_seqlens[b] + t, and the queries
+    attend to cache_seqlens[b] + S_new tokens; ``cache_seqlens`` itself is left
+    unchanged.
     """
-    if k is not None or v is not None:
-        raise NotImplementedError("appending new k/v to the cache is not supported")
+    if (k is None) != (v is None):
+        raise ValueError("k and v must be given together")
     if cache_leftpad is not None or cache_batch_idx is not None:
         raise NotImplementedError("cache_leftpad / cache_batch_idx are not supported")
-    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table)
+    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table, k, v)
     if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q and the caches must share dtype float16 or bfloat16")
     if cache_seqlens.dtype != torch.int32:
@@ -245,10 +253,24 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
-    _check(lib.fa_fwd_kvcache(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
-                              _ptr(block_table), bts, page, nblocks, ns, _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-                              B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
+    if k is None:
+        _check(lib.fa_fwd_kvcache(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                  _ptr(block_table), bts, page, nblocks, ns, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                  B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
+    else:
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("k and v must share the dtype of q")
+        if k.dim() != 4 or k.shape != v.shape or k.shape[0] != B or k.shape[2] != Hkv or k.shape[3] != D:
+            raise ValueError("k and v must be [B, S_new, Hkv, D]")
+        if k.stride(-1) != 1 or v.stride(-1) != 1:
+            raise ValueError("head_dim of k and v must be contiguous")
+        _check(lib.fa_fwd_kvcache_append(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(cache_seqlens), _ptr(block_table), bts, page, nblocks, ns,
+                                         _ptr(k), _ptr(v), k.shape[1], _strides(k, (0, 1, 2)),
+                                         _strides(v, (0, 1, 2)), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                         B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
     return (out, lse) if return_softmax_lse else out
 
 

@@ -47,16 +47,17 @@ constexpr int kOrderMaxB = 2048;    // larger batches are scheduled in their giv
 
 // order[i] = (b, len_b) of the sequence with the i-th largest split length
 // ceil(len_b / num_splits), ties by b.  One workgroup; rank by counting.
-__global__ __launch_bounds__(1024) void decode_order_kernel(const int* __restrict__ lens, int B, int ns,
+// Lengths are lens[b] + add.
+__global__ __launch_bounds__(1024) void decode_order_kernel(const int* __restrict__ lens, int add, int B, int ns,
                                                            int2* __restrict__ order) {
   __shared__ int s_key[kOrderMaxB];
   const int tid = threadIdx.x;
   if (B > kOrderMaxB) {
-    for (int b = tid; b < B; b += blockDim.x) order[b] = make_int2(b, lens[b]);
+    for (int b = tid; b < B; b += blockDim.x) order[b] = make_int2(b, lens[b] + add);
     return;
   }
   for (int b = tid; b < B; b += blockDim.x) {
-    const int l = lens[b];
+    const int l = lens[b] + add;
     s_key[b] = l > 0 ? (l - 1) / ns + 1 : 0;
   }
   __syncthreads();
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(1024) void decode_order_kernel(const int* __restric
       const int kj = s_key[j];
       rank += (kj > key) | ((kj == key) & (j < b));
     }
-    order[rank] = make_int2(b, lens[b]);
+    order[rank] = make_int2(b, lens[b] + add);
   }
 }
 
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   if (!p.order) {
     // B <= 64: rank the sequences here, lane b holding sequence b (lanes past B
     // get key -1 and so ranks B .. 63)
-    const int lb = lane < p.B ? p.cache_seqlens[lane] : 0;
+    const int lb = lane < p.B ? p.cache_seqlens[lane] + p.seqlen_add : 0;
     const int key = lane < p.B ? (lb > 0 ? (lb - 1) / p.num_splits + 1 : 0) : -1;
     int rank = 0;
 #pragma unroll
@@ -531,7 +532,8 @@ hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s) 
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if (cus < 1) cus = 1;
   if (p.order) {
-    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, s, p.cache_seqlens, p.B, p.num_splits, p.order);
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(1024), 0, s, p.cache_seqlens, p.seqlen_add, p.B,
+                       p.num_splits, p.order);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dt == kF16) return D == 64 ? launch_d<F16, 64>(p, cus, s) : launch_d<F16, 128>(p, cus, s);

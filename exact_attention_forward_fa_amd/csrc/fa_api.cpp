@@ -203,11 +203,18 @@ int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits) {
   return (int)n;
 }
 
-fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
-                         const int* cache_seqlens, const int* block_table, int block_table_stride,
-                         int page_size, int num_blocks_or_smax, int num_splits,
-                         void* workspace, size_t workspace_bytes, void* out, float* lse,
-                         int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream) {
+}  // extern "C"
+
+// The decode path of fa_fwd_kvcache and fa_fwd_kvcache_append: optionally
+// append S_new new tokens (k_new/v_new non-null), then split-KV decode over
+// cache_seqlens[b] + S_new tokens and the LSE combine.
+static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void* v_cache,
+                              const int* cache_seqlens, const int* block_table, int block_table_stride,
+                              int page_size, int num_blocks_or_smax, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* out, float* lse,
+                              int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream,
+                              const void* k_new, const void* v_new, int S_new,
+                              const int64_t* kn_stride, const int64_t* vn_stride) {
   fa_status st = check_common(dtype, Hq, Hkv, D);
   if (st) return st;
   if (B < 0 || Sq < 0 || num_blocks_or_smax < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
@@ -220,24 +227,62 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
   if ((Hq / Hkv) * (int64_t)Sq > 16)
     return fail(FA_ERR_UNSUPPORTED, "(Hq/Hkv)*Sq = %lld query rows per kv head; at most 16 are built",
                 (long long)(Hq / Hkv) * Sq);
-  if (B == 0 || Sq == 0) return ok();
-  if (!q || !k_cache || !v_cache || !cache_seqlens || !out || !lse)
-    return fail(FA_ERR_INVALID_ARGUMENT, "null pointer");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return fail(FA_ERR_UNSUPPORTED, "q/k_cache/v_cache must be 16-byte aligned");
-  const int smax_bound = block_table ? block_table_stride * page_size : num_blocks_or_smax;
-  const int ns = fa_kvcache_num_splits(B, Hkv, smax_bound, num_splits);
-  const size_t need = fa_kvcache_workspace_size(B, Sq, Hq, D, ns);
-  if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "null workspace");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (S_new < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative number of new tokens");
+  if (S_new > 0 && (!k_new || !v_new)) return fail(FA_ERR_INVALID_ARGUMENT, "null k_new / v_new");
+  const int64_t knd[3] = {(int64_t)S_new * Hkv * D, (int64_t)Hkv * D, D};
+  const int64_t* kns = kn_stride ? kn_stride : knd;
+  const int64_t* vns = vn_stride ? vn_stride : knd;
+  if (S_new > 0) {
+    for (int i = 0; i < 3; ++i) {
+      if (kns[i] < 0 || vns[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative k_new / v_new stride");
+      if (kns[i] % 8 || vns[i] % 8)
+        return fail(FA_ERR_UNSUPPORTED, "k_new / v_new strides must be multiples of 8 elements");
+    }
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(FA_ERR_UNSUPPORTED, "k_new / v_new must be 16-byte aligned");
+  }
+  if (B == 0 || (Sq == 0 && S_new == 0)) return ok();
+  if (!k_cache || !v_cache || !cache_seqlens) return fail(FA_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FA_ERR_UNSUPPORTED, "k_cache/v_cache must be 16-byte aligned");
+  if (S_new > 0 && num_blocks_or_smax == 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "new tokens for an empty cache");
+  if (S_new > 0 && (int64_t)B * S_new * Hkv * (D / 8) > (int64_t)kMaxGrid * 256)
+    return fail(FA_ERR_UNSUPPORTED, "too many new tokens for one launch");
+  // everything the decode needs is checked before anything is launched
+  int ns = 0;
+  if (Sq > 0) {
+    if (!q || !out || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(q)) return fail(FA_ERR_UNSUPPORTED, "q must be 16-byte aligned");
+    const int smax_bound = block_table ? block_table_stride * page_size : num_blocks_or_smax;
+    ns = fa_kvcache_num_splits(B, Hkv, smax_bound, num_splits);
+    const size_t need = fa_kvcache_workspace_size(B, Sq, Hq, D, ns);
+    if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "null workspace");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(FA_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    // the decode schedule numbers work items (b, split, kv head) and rounds in int
+    if ((int64_t)B * ns * Hkv > (int64_t)1 << 30)
+      return fail(FA_ERR_UNSUPPORTED, "B*num_splits*Hkv = %lld work items; at most 2^30 are built",
+                  (long long)B * ns * Hkv);
+  }
 
-  // the decode schedule numbers work items (b, split, kv head) and rounds in int
-  if ((int64_t)B * ns * Hkv > (int64_t)1 << 30)
-    return fail(FA_ERR_UNSUPPORTED, "B*num_splits*Hkv = %lld work items; at most 2^30 are built",
-                (long long)B * ns * Hkv);
+  hipStream_t s = (hipStream_t)stream;
+  if (S_new > 0) {
+    fa::AppendParams a{};
+    a.k_new = k_new; a.v_new = v_new;
+    a.kn_sb = kns[0]; a.kn_ss = kns[1]; a.kn_sh = kns[2];
+    a.vn_sb = vns[0]; a.vn_ss = vns[1]; a.vn_sh = vns[2];
+    a.k_cache = k_cache; a.v_cache = v_cache;
+    a.cache_seqlens = cache_seqlens;
+    a.block_table = block_table; a.bt_stride = block_table_stride; a.page_size = page_size;
+    a.num_blocks = block_table ? num_blocks_or_smax : 0;
+    a.smax = block_table ? 0 : num_blocks_or_smax;
+    a.B = B; a.S = S_new; a.Hkv = Hkv; a.D = D;
+    hipError_t e = fa::launch_append(a, s);
+    if (e != hipSuccess) return launch_status(e, "append launch");
+  }
+  if (Sq == 0) return ok();
 
   const size_t rows = (size_t)B * Sq * Hq * ns;
   char* ws = static_cast<char*>(workspace);
@@ -251,6 +296,7 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
   // empty cache (every sequence of length 0) gets q as a stand-in
   if (num_blocks_or_smax == 0) { d.k = q; d.v = q; }
   d.cache_seqlens = cache_seqlens;
+  d.seqlen_add = S_new;
   d.block_table = block_table;
   d.bt_stride = block_table_stride;
   d.page_size = block_table ? page_size : num_blocks_or_smax;
@@ -271,7 +317,6 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
   d.causal = opts ? (opts->causal != 0) : 0;
   d.wl = opts ? opts->window_left : -1;
   d.wr = opts ? opts->window_right : -1;
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e = fa::launch_decode((fa::Dtype)dtype, D, d, s);
   if (e != hipSuccess) return launch_status(e, "decode launch");
 
@@ -285,6 +330,30 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
   c.l_sh = Sq; c.l_ss = 1; c.l_sb = (int64_t)Hq * Sq;
   c.B = B; c.S = Sq; c.H = Hq; c.D = D; c.num_splits = ns;
   return launch_status(fa::launch_combine((fa::Dtype)dtype, c, s), "combine launch");
+}
+
+extern "C" {
+
+fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
+                         const int* cache_seqlens, const int* block_table, int block_table_stride,
+                         int page_size, int num_blocks_or_smax, int num_splits,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse,
+                         int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream) {
+  return kvcache_impl(dtype, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), cache_seqlens, block_table,
+                      block_table_stride, page_size, num_blocks_or_smax, num_splits, workspace, workspace_bytes,
+                      out, lse, B, Sq, Hq, Hkv, D, opts, stream, nullptr, nullptr, 0, nullptr, nullptr);
+}
+
+fa_status fa_fwd_kvcache_append(fa_dtype dtype, const void* q, void* k_cache, void* v_cache,
+                                const int* cache_seqlens, const int* block_table, int block_table_stride,
+                                int page_size, int num_blocks_or_smax, int num_splits,
+                                const void* k_new, const void* v_new, int S_new,
+                                const int64_t* kn_stride, const int64_t* vn_stride,
+                                void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream) {
+  return kvcache_impl(dtype, q, k_cache, v_cache, cache_seqlens, block_table, block_table_stride, page_size,
+                      num_blocks_or_smax, num_splits, workspace, workspace_bytes, out, lse, B, Sq, Hq, Hkv, D,
+                      opts, stream, k_new, v_new, S_new, kn_stride, vn_stride);
 }
 
 fa_status fa_combine(const float* out_partial, const float* lse_partial, int B, int S, int H, int D,

@@ -41,6 +41,7 @@ struct DecodeParams {
   const void* k;               // dense [B, Smax, Hkv, D] or pool [P, page, Hkv, D]
   const void* v;
   const int* cache_seqlens;    // [B]
+  int seqlen_add;              // tokens appended by this call: sequence b attends to cache_seqlens[b] + seqlen_add
   const int* block_table;      // [B, bt_stride] or nullptr (dense)
   int bt_stride;
   int page_size;               // paged: tokens per page; dense: Smax
@@ -59,6 +60,22 @@ struct DecodeParams {
   int wl, wr;
 };
 
+// New keys/values [B, S, Hkv, D] written into a KV cache at positions
+// cache_seqlens[b] + t (dense [B, smax, Hkv, D] or pool [num_blocks, page_size, Hkv, D]).
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  int64_t kn_sb, kn_ss, kn_sh;   // element strides of k_new (b, t, head)
+  int64_t vn_sb, vn_ss, vn_sh;
+  void* k_cache;
+  void* v_cache;
+  const int* cache_seqlens;
+  const int* block_table;        // [B, bt_stride] or nullptr (dense)
+  int bt_stride, page_size, num_blocks;
+  int smax;                      // dense: rows per sequence
+  int B, S, Hkv, D;
+};
+
 // LSE-weighted merge of split partials.
 struct CombineParams {
   const float* out_partial;
@@ -75,6 +92,7 @@ struct CombineParams {
 hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s);
 hipError_t launch_combine(Dtype dt, const CombineParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
 // Prefill workgroup shape per head dim: NW waves, each owning RB blocks of 32 query rows.
 #ifndef FA_PREFILL_NW64

@@ -130,6 +130,32 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
                          int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream);
 
 /*
+ * fa_fwd_kvcache with new keys and values appended first ("FlashAttention
+ * 常用接口简单介绍", §3.3: the optional k and v that update the cache).
+ *   k_new, v_new: [B, S_new, Hkv, D] of dtype; kn_stride / vn_stride give the
+ *     element strides of (batch, token, head), NULL = contiguous; strides must
+ *     be multiples of 8 elements and both pointers 16-byte aligned.
+ *   cache_seqlens counts the tokens already cached: token t of sequence b is
+ *     written at cache position cache_seqlens[b] + t (through block_table when
+ *     given), in place in k_cache / v_cache, and the Sq queries then attend to
+ *     cache_seqlens[b] + S_new tokens, bottom-right aligned.  cache_seqlens
+ *     itself is not modified; advancing it is the caller's step.
+ *   The caller guarantees cache_seqlens[b] + S_new fits the cache (Smax, or the
+ *     pages of block_table row b); a new token whose position falls outside the
+ *     cache is not written.
+ *   Sq = 0 only appends.  All other arguments, limits and errors are those of
+ *   fa_fwd_kvcache, which is this call with S_new = 0.  Arguments are checked
+ *   before anything is launched.
+ */
+fa_status fa_fwd_kvcache_append(fa_dtype dtype, const void* q, void* k_cache, void* v_cache,
+                                const int* cache_seqlens, const int* block_table, int block_table_stride,
+                                int page_size, int num_blocks_or_smax, int num_splits,
+                                const void* k_new, const void* v_new, int S_new,
+                                const int64_t* kn_stride, const int64_t* vn_stride,
+                                void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream);
+
+/*
  * Merge split partial results by their log-sum-exp ("FlashAttention 常用接口简单介绍",
  * §3.4 flash_attn_combine).  out_partial [B, S, H, D, num_splits] and
  * lse_partial [B, S, H, num_splits] float32; op_stride (5 entries: b, s, h, d,

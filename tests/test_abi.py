@@ -27,8 +27,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_combine", "fa_kvcache_workspace_size",
-            "fa_kvcache_num_splits", "fa_status_string", "fa_last_error"} <= set(names)
+    assert {"fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_append", "fa_combine",
+            "fa_kvcache_workspace_size", "fa_kvcache_num_splits", "fa_status_string",
+            "fa_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libfa.so"
 
@@ -122,6 +123,28 @@ def test_kvcache_workspace_and_rejects(lib):
     assert kv(bts=0) == 1
 
 
+def test_kvcache_append_rejects(lib):
+    """Every argument error of the append variant is reported before any launch."""
+    ob, keep = _opts()
+    FAKE16 = ctypes.c_void_p(1 << 20)
+
+    def ap(kn=FAKE16, vn=FAKE16, S=3, kst=None, nb=100, ws=FAKE, wsb=1 << 30, Sq=1, bt=FAKE):
+        return lib.fa_fwd_kvcache_append(1, FAKE, FAKE, FAKE, FAKE, bt, 64, 256, nb, 16, kn, vn, S, kst, None,
+                                         ws, wsb, FAKE, FAKE, 4, Sq, 32, 8, 128, ob, None)
+    assert ap(S=-1) == 1                      # negative number of new tokens
+    assert ap(kn=None) == 1                   # new keys missing
+    assert ap(vn=None) == 1
+    assert ap(kn=ctypes.c_void_p((1 << 20) + 2)) == 2             # not 16-byte aligned
+    assert ap(kst=(ctypes.c_int64 * 3)(3 * 8 * 128, 8 * 128, 100)) == 2   # stride not a multiple of 8
+    assert ap(kst=(ctypes.c_int64 * 3)(-8, 8 * 128, 128)) == 1
+    assert ap(nb=0) == 1                      # no room: empty cache
+    assert ap(wsb=100) == 3                   # decode workspace checked before the append runs
+    assert ap(ws=None) == 1
+    assert ap(S=0, Sq=0) == 0                 # nothing to do
+    assert lib.fa_fwd_kvcache_append(1, None, None, None, None, None, 0, 0, 0, 0, None, None, 0, None, None,
+                                     None, 0, None, None, 0, 1, 32, 8, 128, ob, None) == 0   # B = 0
+
+
 def test_combine_rejects(lib):
     f = lambda **k: lib.fa_combine(FAKE, FAKE, 1, 1, 1, k.get("D", 64), k.get("ns", 4), None, None,
                                    k.get("dt", 0), k.get("out", FAKE), None, None, None)
@@ -140,6 +163,8 @@ def test_python_layer_rejects_unsupported_kwargs():
     with pytest.raises(NotImplementedError):
         fa.fwd(q, q, q, return_attn_probs=True)
     with pytest.raises(NotImplementedError):
+        fa.fwd_kvcache(q, q, q, torch.zeros(1, dtype=torch.int32), cache_leftpad=q)
+    with pytest.raises(ValueError):          # new keys without new values
         fa.fwd_kvcache(q, q, q, torch.zeros(1, dtype=torch.int32), k=q)
     with pytest.raises(ValueError):          # CPU tensors: no fallback path exists
         fa.fwd(q, q, q)

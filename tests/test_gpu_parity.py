@@ -414,3 +414,84 @@ def test_decode_running_max_stress(profile):
     torch.cuda.synchronize()
     ro, rl = ref.attention_kvcache(q, k, v, lens)
     check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"decode {profile}")
+
+
+# ------------------------------------------------- KV append (new keys and values)
+
+APPEND = [
+    # (paged, page, B, final lengths, S_new, Sq, Hq, Hkv, D, dtype, causal)
+    (True, 256, 3, [1000, 257, 4097], 1, 1, 8, 2, 128, torch.bfloat16, True),
+    (True, 64, 2, [130, 70], 5, 5, 4, 2, 64, torch.float16, True),        # the new block crosses a page
+    (True, 64, 2, [64, 3], 3, 1, 4, 4, 128, torch.float16, False),        # starts on a page boundary
+    (False, 0, 2, [900, 33], 4, 4, 8, 2, 128, torch.bfloat16, True),
+    (False, 0, 2, [17, 300], 6, 0, 4, 4, 64, torch.float16, False),       # Sq = 0: append only
+]
+
+
+@pytest.mark.parametrize("case", APPEND, ids=lambda c: f"{'paged' + str(c[1]) if c[0] else 'dense'}-S{c[4]}-q{c[5]}-d{c[8]}")
+def test_kvcache_append(case):
+    paged, page, B, final, S, Sq, Hq, Hkv, D, dt, causal = case
+    print("case", case, flush=True)
+    pc = inputs.paged_cache(B, max(Sq, 1), Hq, Hkv, D, dt, seed=600 + sum(final), page_size=page or 64,
+                            lengths=final, tail_fill="nan")
+    g = torch.Generator().manual_seed(601 + S)
+    kn = torch.randn(B, S, Hkv, D, generator=g).to(dt)
+    vn = torch.randn(B, S, Hkv, D, generator=g).to(dt)
+    lens = (pc.cache_seqlens - S).to(torch.int32)
+    q = pc.q[:, :Sq].contiguous()
+    if paged:
+        kc, vc, bt = pc.k_pool, pc.v_pool, pc.block_table
+    else:
+        smax = max(final) + 5
+        kc = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens, smax=smax)
+        vc = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens, smax=smax)
+        kc[:, max(final):] = float("nan")              # rows past every final length
+        vc[:, max(final):] = float("nan")
+        bt = None
+    kg, vg, lg = kc.to(DEV), vc.to(DEV), lens.to(DEV)
+    res = fa.fwd_kvcache(q.to(DEV), kg, vg, lg, block_table=None if bt is None else bt.to(DEV),
+                         k=kn.to(DEV), v=vn.to(DEV), causal=causal, num_splits=3)
+    torch.cuda.synchronize()
+    k2, v2 = ref.kvcache_append(kc, vc, kn, vn, lens, bt, page if paged else None)
+    # the caches after the call: bit for bit, NaN (rows past the lengths) matching any NaN
+    want_k = torch.from_numpy(k2).to(dt)
+    want_v = torch.from_numpy(v2).to(dt)
+    for name, got, want in (("k", kg.cpu(), want_k), ("v", vg.cpu(), want_v)):
+        bad = ((got.view(torch.int16) != want.view(torch.int16)) & ~(got.isnan() & want.isnan())).nonzero()
+        assert bad.shape[0] == 0, (f"{name} cache after append: {bad.shape[0]} elements differ, first at "
+                                   f"{bad[:4].tolist()}: got {[float(got[tuple(i)]) for i in bad[:4].tolist()]} "
+                                   f"want {[float(want[tuple(i)]) for i in bad[:4].tolist()]}")
+    assert torch.equal(lg.cpu(), lens), "cache_seqlens must not change"
+    if Sq:
+        out, lse = res
+        ro, rl = ref.attention_kvcache(q, k2, v2, pc.cache_seqlens, bt, page if paged else None, causal=causal)
+        check(out.cpu(), lse.cpu(), ro, rl, dt, f"append {case}")
+
+
+def test_kvcache_append_then_decode_equals_prefilled_cache():
+    """Two steps of generation with appends give the same result, bit for bit, as
+    decoding against a cache that already holds those tokens."""
+    B, Hq, Hkv, D, dt = 2, 8, 2, 128, torch.bfloat16
+    final = [700, 1300]
+    pc = inputs.paged_cache(B, 1, Hq, Hkv, D, dt, seed=777, page_size=64, lengths=final)
+    kg0, vg0 = pc.k_pool.to(DEV), pc.v_pool.to(DEV)
+    bt = pc.block_table.to(DEV)
+    # reference: the full cache, decoding step 2 (lengths final)
+    ref_out, ref_lse = fa.fwd_kvcache(pc.q.to(DEV), kg0, vg0, pc.cache_seqlens.to(DEV), block_table=bt,
+                                      num_splits=4)
+    # the same pool with the last two tokens blanked, then appended one at a time
+    kg, vg = kg0.clone(), vg0.clone()
+    for b, n in enumerate(final):
+        for t in (n - 2, n - 1):
+            page = int(pc.block_table[b, t // 64])
+            kg[page, t % 64] = 0
+            vg[page, t % 64] = 0
+    for step in (2, 1):
+        lens = (pc.cache_seqlens - step).to(DEV)
+        kn = torch.stack([kg0[int(pc.block_table[b, (n - step) // 64]), (n - step) % 64] for b, n in enumerate(final)])
+        vn = torch.stack([vg0[int(pc.block_table[b, (n - step) // 64]), (n - step) % 64] for b, n in enumerate(final)])
+        out, lse = fa.fwd_kvcache(pc.q.to(DEV), kg, vg, lens, block_table=bt, k=kn[:, None].contiguous(),
+                                  v=vn[:, None].contiguous(), num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(kg, kg0) and torch.equal(vg, vg0)
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
