@@ -11,8 +11,10 @@ Prints ONE JSON line.  value = prefill TFLOP/s over algorithmic FLOPs
 (4·D per allowed (query, key) pair, masked area excluded) divided by the
 prefill kernel's mean duration from HIP events on the launch stream; the
 decode figure (GB/s of algorithmic K/V/q/out/block-table bytes over the
-decode + combine time) rides along in "decode".  "cpu_baseline" times the
-float64 CPU oracle on a bounded sample of the prefill workload.
+decode + combine time) rides along in "decode".  "decode_append" times the
+same decode call with a one-token KV append per sequence (fwd_kvcache with
+k=, v=), after the timed steps.  "cpu_baseline" times the float64 CPU oracle
+on a bounded sample of the prefill workload.
 """
 
 from __future__ import annotations
@@ -189,6 +191,34 @@ def main():
     d_bytes = decode_bytes(dc) if run_d else 0
     gbs = d_bytes / (d_mean * 1e-3) / 1e9
 
+    # decode with a one-token KV append (fwd_kvcache with k=, v=): every
+    # sequence's last cached token is written again from k_new/v_new (its own
+    # values, so the cache is unchanged) and then attended with the rest
+    a_mean = a_bytes = None
+    if run_d:
+        page = dc["page_size"]
+        last = dc["cache_seqlens"].long() - 1
+        pages = dc["block_table"][torch.arange(dB), last // page].long()
+        kn = dc["k_pool"][pages, last % page].unsqueeze(1).contiguous().to(dev)
+        vn = dc["v_pool"][pages, last % page].unsqueeze(1).contiguous().to(dev)
+        lens_before = lens - 1
+
+        def append_step():
+            fa.fwd_kvcache(dq, kp, vp, lens_before, block_table=bt, num_splits=ns, workspace=ws, out=dout,
+                           lse=dlse, k=kn, v=vn)
+        for _ in range(args.warmup):
+            append_step()
+        torch.cuda.synchronize()
+        aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            aev[i][0].record()
+            append_step()
+            aev[i][1].record()
+        torch.cuda.synchronize()
+        a_ms = [e[0].elapsed_time(e[1]) for e in aev]
+        a_mean = sum(a_ms) / len(a_ms)
+        a_bytes = d_bytes + 2 * 2 * kn.numel() * kn.element_size()   # new K/V read + cache rows written
+
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -235,6 +265,10 @@ def main():
                    "ms_min": round(min(d_ms), 5), "bytes": d_bytes, "dtype": "bf16",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": d_traffic}},
+        "decode_append": None if a_mean is None else {
+            "value": round(a_bytes / (a_mean * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_mean": round(a_mean, 5),
+            "bytes": a_bytes, "new_tokens_per_sequence": 1,
+            "extra_us_over_decode": round((a_mean - d_mean) * 1e3, 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None if cpu is None else {kk: cpu[kk] for kk in ("value", "unit", "cores", "kind", "sample")},
