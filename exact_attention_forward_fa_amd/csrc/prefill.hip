@@ -48,13 +48,14 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 // swizzle keeps every LDS read at "one base register + immediate offset":
 //  * K rows of 2D+16 bytes: the 16 lanes of a 16-byte K read hit 16 different
 //    rows, whose starts then fall on 16 distinct 16-byte bank groups;
-//  * V rows of 2D+64 bytes: a transposing read covers 4 rows x 64 bytes per 32
-//    lanes, and the 64-byte row offsets map those rows to 4 disjoint bank ranges.
+//  * V rows of 192 bytes (D = 32, 64, 96) or 2D+64 bytes (D = 128): a transposing
+//    read covers 4 rows x 64 bytes per 32 lanes, and row starts 64 bytes apart
+//    modulo 256 map those rows to 4 disjoint bank ranges.
 template <int D> constexpr int k_stride() { return D + 8; }
 #ifndef FA_PREFILL_VPAD
 #define FA_PREFILL_VPAD 32
 #endif
-template <int D> constexpr int v_stride() { return D + FA_PREFILL_VPAD; }
+template <int D> constexpr int v_stride() { return D + (D == 96 ? 0 : D == 32 ? 64 : FA_PREFILL_VPAD); }
 
 template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
@@ -68,8 +69,11 @@ void prefill_kernel(PrefillParams p) {
   constexpr int DC = D / 16;              // contraction steps of Q K^T
   constexpr int DB = D / 32;              // 32-wide blocks of the output
   constexpr int NT = NW * 64;
-  constexpr int LOADS = BN * CH / NT;     // 16-byte loads per thread per tile, for K and for V
-  static_assert(LOADS * NT == BN * CH, "tile must split evenly over the workgroup");
+  constexpr int LOADS = (BN * CH + NT - 1) / NT;   // 16-byte loads per thread per tile, for K and for V
+  // with D = 32 or 96 the last load round covers only the first waves (a whole
+  // number of them, so the guard is wave-uniform)
+  constexpr bool EVEN = LOADS * NT == BN * CH;
+  static_assert(EVEN || (BN * CH) % 64 == 0, "partial load rounds must end on a wave boundary");
   constexpr bool PLAIN = !SOFTCAP && !ALIBI;
 
   constexpr int KS = k_stride<D>(), VS = v_stride<D>();
@@ -181,6 +185,7 @@ void prefill_kernel(PrefillParams p) {
       const char* vt = (const char*)(vp + (int64_t)j0 * p.v_ss);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
+        if (!EVEN && tid + i * NT >= BN * CH) continue;
         kst[i] = *(const u32x4*)(kt + koff[i]);
         vst[i] = *(const u32x4*)(vt + voff[i]);
       }
@@ -188,6 +193,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+        if (!EVEN && cid >= BN * CH) continue;
         const int j = min(j0 + r, sk - 1);
         kst[i] = *(const u32x4*)(kp + (int64_t)j * p.k_ss + c * 8);
         vst[i] = *(const u32x4*)(vp + (int64_t)j * p.v_ss + c * 8);
@@ -198,6 +204,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+      if (!EVEN && cid >= BN * CH) continue;
       *(u32x4*)(&ksm[buf][r * KS + c * 8]) = kst[i];
       *(u32x4*)(&vsm[buf][r * VS + c * 8]) = vst[i];
     }
@@ -733,20 +740,22 @@ void prefill_pp_kernel(PrefillParams p) {
 // workgroup and 64-key tiles, for both head dims.  (RB = 2 blocks per wave
 // shares every K/V operand read between two MFMAs but needs more than the
 // 256-register budget of two waves per SIMD.)
-template <int D> struct Shape;
+template <int D> struct Shape { static constexpr int NW = 8, RB = 1, BN = 64; };
 template <> struct Shape<64> { static constexpr int NW = FA_PREFILL_NW64, RB = FA_PREFILL_RB64, BN = 64; };
 template <> struct Shape<128> { static constexpr int NW = FA_PREFILL_NW128, RB = FA_PREFILL_RB128, BN = 64; };
 
 int prefill_block_m(int D) {
   if (D >= FA_PREFILL_PINGPONG_MIN_D) return 8 * 32;
-  return D == 64 ? Shape<64>::NW * 32 * Shape<64>::RB : Shape<128>::NW * 32 * Shape<128>::RB;
+  if (D == 64) return Shape<64>::NW * 32 * Shape<64>::RB;
+  if (D == 128) return Shape<128>::NW * 32 * Shape<128>::RB;
+  return 8 * 32;   // D = 32, 96
 }
 
 template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
   using S = Shape<D>;
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
-  if (D >= FA_PREFILL_PINGPONG_MIN_D)
+  if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D)
     hipLaunchKernelGGL((prefill_pp_kernel<E, D, 64, SC, AL>), dim3(grid), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, S::NW, S::RB, SC, AL>), dim3(grid), dim3(S::NW * 64), 0, s, p);
@@ -762,9 +771,18 @@ static hipError_t launch_d(const PrefillParams& p, hipStream_t s) {
   return launch_one<E, D, false, false>(p, s);
 }
 
+template <class E>
+static hipError_t launch_e(int D, const PrefillParams& p, hipStream_t s) {
+  switch (D) {
+    case 32: return launch_d<E, 32>(p, s);
+    case 64: return launch_d<E, 64>(p, s);
+    case 96: return launch_d<E, 96>(p, s);
+    default: return launch_d<E, 128>(p, s);
+  }
+}
+
 hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s) {
-  if (dt == kF16) return D == 64 ? launch_d<F16, 64>(p, s) : launch_d<F16, 128>(p, s);
-  return D == 64 ? launch_d<BF16, 64>(p, s) : launch_d<BF16, 128>(p, s);
+  return dt == kF16 ? launch_e<F16>(D, p, s) : launch_e<BF16>(D, p, s);
 }
 
 }  // namespace fa

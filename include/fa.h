@@ -18,9 +18,11 @@
  *  - Element type: fa_dtype (fp16 or bf16) for q/k/v/out; float32 for lse,
  *    ALiBi slopes and the decode workspace; int32 for cu_seqlens,
  *    cache_seqlens and block_table.
- *  - Head dimension D must be 64 or 128; the head-dim stride is 1 and row
- *    starts must be 16-byte aligned (strides multiples of 8 elements, base
- *    pointers 16-byte aligned).
+ *  - Head dimension D: 32, 64, 96 or 128 for fa_fwd / fa_fwd_varlen, 64 or 128
+ *    for the KV-cache calls, any D for fa_combine; other values return
+ *    FA_ERR_UNSUPPORTED.  The head-dim stride is 1 and row starts must be
+ *    16-byte aligned (strides multiples of 8 elements, base pointers 16-byte
+ *    aligned).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on that stream and returns without synchronising; results
  *    are valid once the stream has reached that point.

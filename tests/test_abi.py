@@ -61,7 +61,7 @@ def fwd(lib, dtype=0, B=1, Sq=8, Sk=8, Hq=2, Hkv=2, D=64, ptrs=None, strides=Non
     (dict(Hq=3, Hkv=2), 1),
     (dict(Hkv=0), 1),
     (dict(D=0), 1),
-    (dict(D=96), 2),
+    (dict(D=80), 2),
     (dict(D=256), 2),
     (dict(B=-1), 1),
     (dict(Sk=-3), 1),
@@ -120,6 +120,8 @@ def test_kvcache_workspace_and_rejects(lib):
     assert kv(Hq=32, Hkv=1) == 2              # 32 query rows per kv head > 16
     assert kv(Sq=5) == 2                      # 4 * 5 = 20 rows > 16
     assert kv(page=0) == 1
+    assert lib.fa_fwd_kvcache(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 100, 16, FAKE, 1 << 30, FAKE, FAKE,
+                              4, 1, 32, 8, 96, ob, None) == 2   # head dims 32/96: prefill only
     assert kv(bts=0) == 1
 
 

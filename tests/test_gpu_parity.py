@@ -159,6 +159,13 @@ EDGE = [
     (2, 300, 300, 4, 4, 128, torch.float16, dict()),                     # plain D=128 fp16, non-causal
     (1, 260, 200, 4, 2, 64, torch.bfloat16, dict(alibi=True, window=(50, 20))),
     (1, 220, 150, 4, 1, 64, torch.float16, dict(alibi=True, softcap=10.0, causal=True)),
+    # head dims 32 and 96
+    (1, 200, 300, 4, 2, 32, torch.float16, dict(causal=True)),
+    (2, 130, 130, 4, 4, 32, torch.bfloat16, dict(window=(20, 5), softcap=5.0)),
+    (1, 257, 300, 4, 2, 96, torch.float16, dict()),
+    (1, 300, 200, 2, 1, 96, torch.bfloat16, dict(causal=True, alibi=True)),
+    (1, 190, 250, 4, 2, 96, torch.float16, dict(softcap=10.0, window=(60, 0))),
+    (2, 520, 520, 2, 2, 32, torch.float16, dict(causal=True)),              # several q-tiles, ragged tail
 ]
 
 
@@ -226,6 +233,15 @@ def test_paged_decode_edge_cases(page, lens, ns, sq, fill, D, dt):
     vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
     b = run_paged(c, block_table=False, dense=(kd, vd), num_splits=ns, causal=True)
     assert torch.equal(out, b[0]) and torch.equal(lse, b[1])
+
+
+@pytest.mark.parametrize("D,dt", [(32, torch.bfloat16), (96, torch.float16)])
+def test_varlen_head_dims_32_96(D, dt):
+    q, k, v, cq, ck = inputs.varlen_pack([300, 1, 517], [400, 90, 517], 4, 2, D, dt, seed=830 + D)
+    out, lse = fa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cq.to(DEV), ck.to(DEV), 517, 517, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention_varlen(q, k, v, cq, ck, causal=True)
+    check(out.cpu(), lse.cpu(), ro, rl, dt, f"varlen D={D}")
 
 
 def test_varlen_options_d128():
