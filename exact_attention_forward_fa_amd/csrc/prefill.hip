@@ -58,7 +58,7 @@ template <int D> constexpr int k_stride() { return D + 8; }
 template <int D> constexpr int v_stride() { return D + (D == 96 ? 0 : D == 32 ? 64 : FA_PREFILL_VPAD); }
 
 template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -605,6 +605,9 @@ void prefill_pp_kernel(PrefillParams p) {
   if (grp == 1) barrier();                 // group 1 runs one phase behind
 
   int st_q = 0;                            // stage of tile j (K read by this GEMM phase)
+  // not unrolled: copies of the loop body for the three stages would not fit
+  // the register budget (the plain and ALiBi-only variants then spill)
+#pragma nounroll
   for (int j = 0; j <= n_t; ++j) {
     const int st_p = st_q == 0 ? 2 : st_q - 1;      // stage of tile j-1 (V read by P V)
     const int st_w = st_q == 2 ? 0 : st_q + 1;      // stage of tile j+1 (written now)
@@ -741,13 +744,17 @@ void prefill_pp_kernel(PrefillParams p) {
 // shares every K/V operand read between two MFMAs but needs more than the
 // 256-register budget of two waves per SIMD.)
 template <int D> struct Shape { static constexpr int NW = 8, RB = 1, BN = 64; };
+// D = 256: O alone takes 128 registers per lane, so one wave per SIMD (4 per
+// workgroup) with up to 512 registers, and 32-key tiles to bound the staging
+template <> struct Shape<256> { static constexpr int NW = 4, RB = 1, BN = 32; };
 template <> struct Shape<64> { static constexpr int NW = FA_PREFILL_NW64, RB = FA_PREFILL_RB64, BN = 64; };
 template <> struct Shape<128> { static constexpr int NW = FA_PREFILL_NW128, RB = FA_PREFILL_RB128, BN = 64; };
 
 int prefill_block_m(int D) {
-  if (D >= FA_PREFILL_PINGPONG_MIN_D) return 8 * 32;
+  if (D >= FA_PREFILL_PINGPONG_MIN_D && D <= 128) return 8 * 32;
   if (D == 64) return Shape<64>::NW * 32 * Shape<64>::RB;
   if (D == 128) return Shape<128>::NW * 32 * Shape<128>::RB;
+  if (D == 256) return Shape<256>::NW * 32 * Shape<256>::RB;
   return 8 * 32;   // D = 32, 96
 }
 
@@ -755,7 +762,7 @@ template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
   using S = Shape<D>;
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
-  if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D)
+  if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D && D <= 128)
     hipLaunchKernelGGL((prefill_pp_kernel<E, D, 64, SC, AL>), dim3(grid), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, S::NW, S::RB, SC, AL>), dim3(grid), dim3(S::NW * 64), 0, s, p);
@@ -777,6 +784,7 @@ static hipError_t launch_e(int D, const PrefillParams& p, hipStream_t s) {
     case 32: return launch_d<E, 32>(p, s);
     case 64: return launch_d<E, 64>(p, s);
     case 96: return launch_d<E, 96>(p, s);
+    case 256: return launch_d<E, 256>(p, s);
     default: return launch_d<E, 128>(p, s);
   }
 }

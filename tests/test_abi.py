@@ -62,7 +62,7 @@ def fwd(lib, dtype=0, B=1, Sq=8, Sk=8, Hq=2, Hkv=2, D=64, ptrs=None, strides=Non
     (dict(Hkv=0), 1),
     (dict(D=0), 1),
     (dict(D=80), 2),
-    (dict(D=256), 2),
+    (dict(D=512), 2),
     (dict(B=-1), 1),
     (dict(Sk=-3), 1),
     (dict(wl=-2), 1),

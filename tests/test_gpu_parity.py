@@ -166,6 +166,10 @@ EDGE = [
     (1, 300, 200, 2, 1, 96, torch.bfloat16, dict(causal=True, alibi=True)),
     (1, 190, 250, 4, 2, 96, torch.float16, dict(softcap=10.0, window=(60, 0))),
     (2, 520, 520, 2, 2, 32, torch.float16, dict(causal=True)),              # several q-tiles, ragged tail
+    # head dim 256
+    (1, 300, 333, 2, 1, 256, torch.bfloat16, dict(causal=True)),
+    (1, 130, 200, 4, 2, 256, torch.float16, dict(softcap=20.0, alibi=True, window=(64, 16))),
+    (2, 77, 77, 2, 2, 256, torch.float16, dict()),
 ]
 
 
