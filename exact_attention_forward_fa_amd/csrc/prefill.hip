@@ -751,7 +751,7 @@ template <> struct Shape<64> { static constexpr int NW = FA_PREFILL_NW64, RB = F
 template <> struct Shape<128> { static constexpr int NW = FA_PREFILL_NW128, RB = FA_PREFILL_RB128, BN = 64; };
 
 int prefill_block_m(int D) {
-  if (D >= FA_PREFILL_PINGPONG_MIN_D && D <= 128) return 8 * 32;
+  if (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128)) return 8 * 32;
   if (D == 64) return Shape<64>::NW * 32 * Shape<64>::RB;
   if (D == 128) return Shape<128>::NW * 32 * Shape<128>::RB;
   if (D == 256) return Shape<256>::NW * 32 * Shape<256>::RB;
@@ -762,7 +762,7 @@ template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
   using S = Shape<D>;
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
-  if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D && D <= 128)
+  if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128))
     hipLaunchKernelGGL((prefill_pp_kernel<E, D, 64, SC, AL>), dim3(grid), dim3(512), 0, s, p);
   else
     hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, S::NW, S::RB, SC, AL>), dim3(grid), dim3(S::NW * 64), 0, s, p);
