@@ -42,6 +42,8 @@ namespace fa {
 #define FA_DECODE_WPE 1
 #endif
 constexpr int kDecodeChunk = FA_DECODE_CHUNK;    // tokens per pipeline step
+// D = 256 halves the chunk: a 64-token chunk of K and V would need 256 registers per lane
+template <int D> constexpr int decode_chunk() { return D >= 256 ? kDecodeChunk / 2 : kDecodeChunk; }
 constexpr float kTauD = 8.f;        // lazy-rescale threshold (log2 units)
 constexpr int kOrderMaxB = 2048;    // larger batches are scheduled in their given order
 
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   using T = typename E::T;
   using V8 = typename E::V8;
   using V2 = typename E::V2;
-  constexpr int C = kDecodeChunk;
+  constexpr int C = decode_chunk<D>();
   constexpr int KSTEP = D / 32;           // MFMA K-steps of Q K^T
   constexpr int DBK = D / 16;             // 16-wide d blocks of O^T
   constexpr int VROW = D + 16;            // V LDS row stride (elements): conflict-free transposing reads
@@ -521,7 +523,7 @@ static hipError_t launch_dm(const DecodeParams& p, int cus, hipStream_t s) {
 template <class E, int D>
 static hipError_t launch_d(const DecodeParams& p, int cus, hipStream_t s) {
   if (!p.block_table) return launch_dm<E, D, 0>(p, cus, s);
-  if (p.page_size >= kDecodeChunk) return launch_dm<E, D, 1>(p, cus, s);
+  if (p.page_size >= decode_chunk<D>()) return launch_dm<E, D, 1>(p, cus, s);
   return launch_dm<E, D, 2>(p, cus, s);
 }
 
@@ -536,8 +538,12 @@ hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s) 
                        p.num_splits, p.order);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (dt == kF16) return D == 64 ? launch_d<F16, 64>(p, cus, s) : launch_d<F16, 128>(p, cus, s);
-  return D == 64 ? launch_d<BF16, 64>(p, cus, s) : launch_d<BF16, 128>(p, cus, s);
+  switch (D) {
+    case 32: return dt == kF16 ? launch_d<F16, 32>(p, cus, s) : launch_d<BF16, 32>(p, cus, s);
+    case 64: return dt == kF16 ? launch_d<F16, 64>(p, cus, s) : launch_d<BF16, 64>(p, cus, s);
+    case 256: return dt == kF16 ? launch_d<F16, 256>(p, cus, s) : launch_d<BF16, 256>(p, cus, s);
+    default: return dt == kF16 ? launch_d<F16, 128>(p, cus, s) : launch_d<BF16, 128>(p, cus, s);
+  }
 }
 
 }  // namespace fa

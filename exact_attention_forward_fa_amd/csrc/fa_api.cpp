@@ -48,7 +48,7 @@ fa_status check_opts(const fa_attn_opts* o, int D, float* scale_out) {
   return FA_OK;
 }
 
-// prefill: D in {32, 64, 96, 128, 256}; decode: D in {64, 128}
+// prefill: D in {32, 64, 96, 128, 256}; decode: D in {32, 64, 128, 256}
 fa_status check_common(int dtype, int Hq, int Hkv, int D, bool prefill) {
   if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
   if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
@@ -56,7 +56,8 @@ fa_status check_common(int dtype, int Hq, int Hkv, int D, bool prefill) {
   if (D <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "head_dim must be positive (D=%d)", D);
   if (prefill && D != 32 && D != 64 && D != 96 && D != 128 && D != 256)
     return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built (32, 64, 96, 128 or 256)", D);
-  if (!prefill && D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built for decode (64 or 128)", D);
+  if (!prefill && D != 32 && D != 64 && D != 128 && D != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built for decode (32, 64, 128 or 256)", D);
   return FA_OK;
 }
 

@@ -291,6 +291,28 @@ def test_paged_decode_options(page, Hq, Hkv, sq, D, dt, ns, opts):
     assert torch.equal(out, b[0]) and torch.equal(lse, b[1])
 
 
+@pytest.mark.parametrize("D,dt,page,paged", [(32, torch.float16, 64, True), (32, torch.bfloat16, 0, False),
+                                             (256, torch.bfloat16, 256, True), (256, torch.float16, 16, True),
+                                             (256, torch.bfloat16, 0, False)])
+def test_decode_head_dims_32_256(D, dt, page, paged):
+    print("case decode D", D, dt, page, paged, flush=True)
+    lens = [700, 33, 1500]
+    pc = inputs.paged_cache(3, 2, 8, 2, D, dt, seed=900 + D + page, page_size=page or 64, lengths=lens,
+                            tail_fill="nan")
+    if paged:
+        out, lse = fa.fwd_kvcache(pc.q.to(DEV), pc.k_pool.to(DEV), pc.v_pool.to(DEV), pc.cache_seqlens.to(DEV),
+                                  block_table=pc.block_table.to(DEV), num_splits=5, causal=True)
+    else:
+        kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
+        vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
+        out, lse = fa.fwd_kvcache(pc.q.to(DEV), kd.to(DEV), vd.to(DEV), pc.cache_seqlens.to(DEV), num_splits=5,
+                                  causal=True)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, page or 64,
+                                   causal=True)
+    check(out.cpu(), lse.cpu(), ro, rl, dt, f"decode D={D} page={page} paged={paged}")
+
+
 def test_paged_decode_many_sequences():
     # more than 64 sequences: the schedule order comes from its own kernel
     lens = [int(x) for x in np.random.default_rng(80).integers(0, 400, 80)]
@@ -445,6 +467,8 @@ APPEND = [
     (True, 64, 2, [64, 3], 3, 1, 4, 4, 128, torch.float16, False),        # starts on a page boundary
     (False, 0, 2, [900, 33], 4, 4, 8, 2, 128, torch.bfloat16, True),
     (False, 0, 2, [17, 300], 6, 0, 4, 4, 64, torch.float16, False),       # Sq = 0: append only
+    (True, 64, 2, [130, 70], 2, 2, 4, 2, 256, torch.bfloat16, True),
+    (False, 0, 2, [40, 9], 3, 1, 4, 4, 32, torch.float16, False),
 ]
 
 
