@@ -521,3 +521,19 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     assert not _brute_agrees(dict())
     monkeypatch.setattr(ref, "_softmax_rows", good_soft)
     assert _brute_agrees(dict(causal=True, alibi=True, softcap=1.0))
+
+
+def test_fp8_e4m3_decoding_matches_the_format_definition():
+    """The oracle reads fp8 inputs through torch's float8_e4m3fn decoding; pin it to
+    the OCP e4m3 definition: 1 sign, 4 exponent (bias 7) and 3 mantissa bits,
+    subnormals at exponent 0, and S.1111.111 the only NaN (no infinities)."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    got = ref._f64(codes.view(torch.float8_e4m3fn))
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            assert np.isnan(got[c]), c
+            continue
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        assert got[c] == (-mag if s else mag), (c, got[c], mag)
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
