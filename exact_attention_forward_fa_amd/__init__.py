@@ -59,6 +59,8 @@ def load_library():
     OP = ctypes.POINTER(_Opts)
     lib.fa_fwd.argtypes = [I, P, P, P, P, P, I, I, I, I, I, I, I64P, I64P, I64P, I64P, OP, P]
     lib.fa_fwd.restype = I
+    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I64P, I64P, I64P, I64P, F, F, F, OP, P]
+    lib.fa_fwd_fp8.restype = I
     lib.fa_fwd_varlen.argtypes = [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I64P, I64P, I64P, I64P, OP, P]
     lib.fa_fwd_varlen.restype = I
     lib.fa_kvcache_workspace_size.argtypes = [I, I, I, I, I]
@@ -135,14 +137,22 @@ def _unsupported_kwargs(dropout_p=0.0, return_attn_probs=False):
 
 
 def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None,
-        out=None, lse=None, dropout_p=0.0, deterministic=False, return_attn_probs=False):
+        out=None, lse=None, dropout_p=0.0, deterministic=False, return_attn_probs=False,
+        q_descale=1.0, k_descale=1.0, v_descale=1.0):
     """Dense forward.  q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] fp16/bf16 on the GPU (D stride 1).
 
     Returns (out [B,Sq,Hq,D], softmax_lse [B,Hq,Sq] float32).  ``deterministic``
     is accepted and ignored: the forward is deterministic.
+
+    float8_e4m3fn q, k, v (D 64 or 128) run the fp8 kernel and return bf16
+    out; ``q_descale`` / ``k_descale`` / ``v_descale`` are per-tensor factors
+    of the dequantised values (1 for a direct conversion).
     """
     _unsupported_kwargs(dropout_p, return_attn_probs)
     _need_gpu(q, k, v)
+    if q.dtype == torch.float8_e4m3fn:
+        return _fwd_fp8(q, k, v, softmax_scale, causal, window_size, softcap, alibi_slopes, out, lse,
+                        q_descale, k_descale, v_descale)
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float16 or bfloat16")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
@@ -162,6 +172,33 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), softcap
     _check(lib.fa_fwd(_DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                       B, Sq, Sk, Hq, Hkv, D, _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)),
                       _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)), ob, _stream(q.device)))
+    return out, lse
+
+
+def _fwd_fp8(q, k, v, softmax_scale, causal, window_size, softcap, alibi_slopes, out, lse,
+             q_descale, k_descale, v_descale):
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float8_e4m3fn")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("expected q [B,Sq,Hq,D] and k, v [B,Sk,Hkv,D]")
+    if q.stride(-1) != 1 or k.stride(-1) != 1 or v.stride(-1) != 1:
+        raise ValueError("head_dim must be contiguous")
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("batch / head_dim mismatch")
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16:
+        raise ValueError("fp8 inputs give a bfloat16 out")
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    _check(lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
+                          _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)), _strides(v, (0, 1, 2)),
+                          _strides(out, (0, 1, 2)), float(q_descale), float(k_descale), float(v_descale),
+                          ob, _stream(q.device)))
     return out, lse
 
 

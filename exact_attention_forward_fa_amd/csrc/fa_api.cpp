@@ -71,6 +71,7 @@ fa_status check_strides(const char* name, const int64_t* s, int n) {
 
 void fill_opts(fa::PrefillParams& p, const fa_attn_opts* o, float scale) {
   p.scale = scale;
+  p.out_scale = 1.f;
   p.softcap = o ? o->softcap : 0.f;
   p.alibi = o ? o->alibi_slopes : nullptr;
   p.causal = o ? (o->causal != 0) : 0;
@@ -141,6 +142,53 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   p.n_qtiles = (int)nqt;
   p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
   return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "prefill launch");
+}
+
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                     const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                     const int64_t* o_stride, float q_descale, float k_descale, float v_descale,
+                     const fa_attn_opts* opts, void* stream) {
+  fa_status st = check_common(FA_BF16, Hq, Hkv, D, true);
+  if (st) return st;
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 head_dim %d not built (64 or 128)", D);
+  if (B < 0 || Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Sk=%d)", B, Sq, Sk);
+  if (!(q_descale > 0.f) || !(k_descale > 0.f) || !(v_descale > 0.f) || !std::isfinite(q_descale) ||
+      !std::isfinite(k_descale) || !std::isfinite(v_descale))
+    return fail(FA_ERR_INVALID_ARGUMENT, "descale factors must be positive and finite");
+  float scale;
+  if ((st = check_opts(opts, D, &scale))) return st;
+  if (B == 0 || Sq == 0) return ok();
+  if (!q || !k || !v || !out || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(FA_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
+  const int64_t qd[3] = {(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
+  const int64_t kd[3] = {(int64_t)Sk * Hkv * D, (int64_t)Hkv * D, D};
+  const int64_t* qs = q_stride ? q_stride : qd;
+  const int64_t* ks = k_stride ? k_stride : kd;
+  const int64_t* vs = v_stride ? v_stride : kd;
+  const int64_t* os = o_stride ? o_stride : qd;
+  if ((st = check_strides("q", qs, 3)) || (st = check_strides("k", ks, 3)) || (st = check_strides("v", vs, 3)) ||
+      (st = check_strides("out", os, 3)))
+    return st;
+  const int bm = fa::prefill_block_m_fp8(D);
+  const int64_t nqt = (Sq + bm - 1) / bm;
+  if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+
+  fa::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  p.q_sb = qs[0]; p.q_ss = qs[1]; p.q_sh = qs[2];
+  p.k_sb = ks[0]; p.k_ss = ks[1]; p.k_sh = ks[2];
+  p.v_sb = vs[0]; p.v_ss = vs[1]; p.v_sh = vs[2];
+  p.o_sb = os[0]; p.o_ss = os[1]; p.o_sh = os[2];
+  p.lse_sb = (int64_t)Hq * Sq; p.lse_sh = Sq;
+  p.cu_seqlens_q = nullptr; p.cu_seqlens_k = nullptr;
+  p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  fill_opts(p, opts, scale * q_descale * k_descale);   // scores of the dequantised q and k
+  p.out_scale = v_descale;
+  p.n_qtiles = (int)nqt;
+  p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
+  return launch_status(fa::launch_prefill_fp8(D, p, (hipStream_t)stream), "fp8 prefill launch");
 }
 
 fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void* v, void* out, float* lse,

@@ -26,7 +26,8 @@ struct PrefillParams {
   const int* cu_seqlens_k;
   int B, Sq, Sk;               // dense sizes; for varlen Sq/Sk hold max_seqlen_q/k
   int Hq, Hkv, group;          // group = Hq / Hkv
-  float scale;                 // softmax scale
+  float scale;                 // softmax scale (for fp8 inputs times the q and k descales)
+  float out_scale;             // out = out_scale * sum_j p_j v_j / sum_j p_j (fp8: the v descale; else 1)
   float softcap;               // 0 = off
   const float* alibi;          // [Hq] slopes or nullptr
   int causal;
@@ -90,6 +91,9 @@ struct CombineParams {
 };
 
 hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s);
+// fp8 e4m3 q/k/v, bf16 out; D in {64, 128}
+hipError_t launch_prefill_fp8(int D, const PrefillParams& p, hipStream_t s);
+int prefill_block_m_fp8(int D);
 hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s);
 hipError_t launch_combine(Dtype dt, const CombineParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);

@@ -24,6 +24,8 @@
 //  * scale·log2(e) is folded into the exp2 argument (one FMA + v_exp_f32 per score).
 //  * tiles that are fully masked for a wave are skipped; mask arithmetic runs only
 //    on tiles that straddle a mask edge.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -57,12 +59,17 @@ template <int D> constexpr int k_stride() { return D + 8; }
 #endif
 template <int D> constexpr int v_stride() { return D + (D == 96 ? 0 : D == 32 ? 64 : FA_PREFILL_VPAD); }
 
-template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI>
+template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI, bool F8 = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
   using V2 = typename E::V2;
+  // F8: q, k, v are fp8 e4m3 (OCP); Q K^T runs on the fp8 MFMA, V is widened
+  // exactly to bf16 (T) on its way into LDS, and P V, out and lse are as for bf16
+  using TI = std::conditional_t<F8, uint8_t, T>;          // element type of q, k, v
+  using QV = std::conditional_t<F8, long, V8>;            // 8-element operand of Q K^T
+  using KST = std::conditional_t<F8, u32x2, u32x4>;       // 8 staged elements of K or V
   constexpr int BM = NW * 32 * RB;        // query rows per workgroup
   constexpr int CH = D / 8;               // 16-byte chunks per row
   constexpr int KB = BN / 32;             // 32-key blocks per tile
@@ -77,6 +84,9 @@ void prefill_kernel(PrefillParams p) {
   constexpr bool PLAIN = !SOFTCAP && !ALIBI;
 
   constexpr int KS = k_stride<D>(), VS = v_stride<D>();
+  // K row stride in elements of TI: fp8 rows of D+8 bytes keep the 8-byte operand
+  // reads of 16 lanes on distinct banks
+  constexpr int KSI = F8 ? D + 8 : KS;
   __shared__ __attribute__((aligned(16))) T ksm[2][BN * KS];   // K tiles, double-buffered
   __shared__ __attribute__((aligned(16))) T vsm[2][BN * VS];   // V tiles
 
@@ -104,9 +114,9 @@ void prefill_kernel(PrefillParams p) {
   if (m0 >= sq) return;
 
   const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
-  const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
-  const T* kp = (const T*)p.k + bq * p.k_sb + (int64_t)kbase * p.k_ss + (int64_t)hk * p.k_sh;
-  const T* vp = (const T*)p.v + bq * p.v_sb + (int64_t)kbase * p.v_ss + (int64_t)hk * p.v_sh;
+  const TI* qp = (const TI*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
+  const TI* kp = (const TI*)p.k + bq * p.k_sb + (int64_t)kbase * p.k_ss + (int64_t)hk * p.k_sh;
+  const TI* vp = (const TI*)p.v + bq * p.v_sb + (int64_t)kbase * p.v_ss + (int64_t)hk * p.v_sh;
   T* op = (T*)p.out + bq * p.o_sb + (int64_t)qbase * p.o_ss + (int64_t)hq * p.o_sh;
   float* lp = p.lse + bq * p.lse_sb + (int64_t)hq * p.lse_sh + qbase;
 
@@ -147,13 +157,13 @@ void prefill_kernel(PrefillParams p) {
   }
 
   // ---- Q operand (B of S^T = K Q^T): lane holds row qrow, d = 16*dc + 8*hi .. +7
-  V8 qr[RB][DC];
+  QV qr[RB][DC];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      if (row_ok[rb]) qr[rb][dc] = *(const V8*)(qp + (int64_t)qrow[rb] * p.q_ss + dc * 16 + hi * 8);
-      else qr[rb][dc] = V8{};
+      if (row_ok[rb]) qr[rb][dc] = *(const QV*)(qp + (int64_t)qrow[rb] * p.q_ss + dc * 16 + hi * 8);
+      else qr[rb][dc] = QV{};
     }
 
   float slope_l2 = 0.f, ipf[RB];
@@ -169,13 +179,13 @@ void prefill_kernel(PrefillParams p) {
   // real row; their scores are masked, so their values only ever meet p = 0)
   // Whole tiles are addressed as a scalar tile base plus a fixed 32-bit byte offset
   // per lane; the last, partial tile clamps row by row.
-  u32x4 kst[LOADS], vst[LOADS];
+  KST kst[LOADS], vst[LOADS];
   uint32_t koff[LOADS], voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
-    koff[i] = (uint32_t)(r * p.k_ss + c * 8) * (uint32_t)sizeof(T);
-    voff[i] = (uint32_t)(r * p.v_ss + c * 8) * (uint32_t)sizeof(T);
+    koff[i] = (uint32_t)(r * p.k_ss + c * 8) * (uint32_t)sizeof(TI);
+    voff[i] = (uint32_t)(r * p.v_ss + c * 8) * (uint32_t)sizeof(TI);
   }
   const bool off32 = p.k_ss >= 0 && p.v_ss >= 0 && p.k_ss < (1 << 24) / BN && p.v_ss < (1 << 24) / BN;
   auto gload = [&](int tile) __attribute__((always_inline)) {
@@ -186,8 +196,8 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         if (!EVEN && tid + i * NT >= BN * CH) continue;
-        kst[i] = *(const u32x4*)(kt + koff[i]);
-        vst[i] = *(const u32x4*)(vt + voff[i]);
+        kst[i] = *(const KST*)(kt + koff[i]);
+        vst[i] = *(const KST*)(vt + voff[i]);
       }
     } else {
 #pragma unroll
@@ -195,8 +205,8 @@ void prefill_kernel(PrefillParams p) {
         const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
         if (!EVEN && cid >= BN * CH) continue;
         const int j = min(j0 + r, sk - 1);
-        kst[i] = *(const u32x4*)(kp + (int64_t)j * p.k_ss + c * 8);
-        vst[i] = *(const u32x4*)(vp + (int64_t)j * p.v_ss + c * 8);
+        kst[i] = *(const KST*)(kp + (int64_t)j * p.k_ss + c * 8);
+        vst[i] = *(const KST*)(vp + (int64_t)j * p.v_ss + c * 8);
       }
     }
   };
@@ -205,8 +215,21 @@ void prefill_kernel(PrefillParams p) {
     for (int i = 0; i < LOADS; ++i) {
       const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
       if (!EVEN && cid >= BN * CH) continue;
-      *(u32x4*)(&ksm[buf][r * KS + c * 8]) = kst[i];
-      *(u32x4*)(&vsm[buf][r * VS + c * 8]) = vst[i];
+      *(KST*)(reinterpret_cast<TI*>(ksm[buf]) + r * KSI + c * 8) = kst[i];
+      if constexpr (F8) {
+        // 8 fp8 values -> 8 bf16 (exact: every e4m3 value is a bf16 value)
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vst[i][h], false);
+          const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vst[i][h], true);
+          w[2 * h] = __builtin_bit_cast(uint32_t, E::pack(lo[0], lo[1]));
+          w[2 * h + 1] = __builtin_bit_cast(uint32_t, E::pack(hi2[0], hi2[1]));
+        }
+        *(u32x4*)(&vsm[buf][r * VS + c * 8]) = w;
+      } else {
+        *(u32x4*)(&vsm[buf][r * VS + c * 8]) = vst[i];
+      }
     }
   };
 
@@ -233,14 +256,17 @@ void prefill_kernel(PrefillParams p) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[rb][kb] = f32x16{};
-    const T* kbase = Ks + l32 * KS + hi * 8;
+    const TI* kbase = reinterpret_cast<const TI*>(Ks) + l32 * KSI + hi * 8;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const V8 a = *(const V8*)(kbase + kb * 32 * KS + dc * 16);
+        const QV a = *(const QV*)(kbase + kb * 32 * KSI + dc * 16);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = E::mfma32(a, qr[rb][dc], s[rb][kb]);
+        for (int rb = 0; rb < RB; ++rb) {
+          if constexpr (F8) s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, qr[rb][dc], s[rb][kb], 0, 0, 0);
+          else s[rb][kb] = E::mfma32(a, qr[rb][dc], s[rb][kb]);
+        }
       }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -453,7 +479,7 @@ void prefill_kernel(PrefillParams p) {
     const float lt = sum_halves(l[rb]);
     const float lxt = sum_halves(lx[rb]);
     if (row_ok[rb]) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
       T* orow = op + (int64_t)qrow[rb] * p.o_ss;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -787,6 +813,29 @@ static hipError_t launch_e(int D, const PrefillParams& p, hipStream_t s) {
     case 256: return launch_d<E, 256>(p, s);
     default: return launch_d<E, 128>(p, s);
   }
+}
+
+// fp8 inputs: the main kernel (8 waves of 32 rows, 64-key tiles) for both head dims
+int prefill_block_m_fp8(int) { return 8 * 32; }
+
+template <int D, bool SC, bool AL>
+static hipError_t launch_f8(const PrefillParams& p, hipStream_t s) {
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
+  hipLaunchKernelGGL((prefill_kernel<BF16, D, 64, 8, 1, SC, AL, true>), dim3(grid), dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_f8d(const PrefillParams& p, hipStream_t s) {
+  const bool sc = p.softcap > 0.f, al = p.alibi != nullptr;
+  if (sc && al) return launch_f8<D, true, true>(p, s);
+  if (sc) return launch_f8<D, true, false>(p, s);
+  if (al) return launch_f8<D, false, true>(p, s);
+  return launch_f8<D, false, false>(p, s);
+}
+
+hipError_t launch_prefill_fp8(int D, const PrefillParams& p, hipStream_t s) {
+  return D == 64 ? launch_f8d<64>(p, s) : launch_f8d<128>(p, s);
 }
 
 hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s) {

@@ -80,6 +80,28 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
                  const int64_t* o_stride, const fa_attn_opts* opts, void* stream);
 
 /*
+ * Dense forward on fp8 inputs ("optimizing-attention-flash" skill page, workflow
+ * three: q, k and v converted to float8_e4m3fn and passed to the forward).
+ *   q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] in OCP fp8 e4m3 (float8_e4m3fn, one
+ *   byte per element); out [B, Sq, Hq, D] bf16; lse [B, Hq, Sq] float32.
+ *   The pages give no scaling recipe.  Reading: each tensor carries one
+ *   positive descale factor (the real value is code value * descale; 1 when the
+ *   tensor was converted directly, as on the pages), and the result is the
+ *   exact attention of the dequantised tensors: scores are
+ *   softmax_scale * q_descale * k_descale * (q . k), out is v_descale times
+ *   the softmax average of the v codes, lse is of the dequantised scores.
+ *   Q Kᵀ runs on the fp8 MFMA with fp32 accumulation (exact products); V is
+ *   widened exactly to bf16 and P rounded to bf16 for P V, as in the bf16 path.
+ *   D is 64 or 128.  Strides, alignment, options and errors are those of
+ *   fa_fwd; strides count elements (bytes here) and must be multiples of 8.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                     const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                     const int64_t* o_stride, float q_descale, float k_descale, float v_descale,
+                     const fa_attn_opts* opts, void* stream);
+
+/*
  * Packed variable-length forward ("FlashAttention 常用接口简单介绍", §3.2).
  *   q [total_q, Hq, D], k/v [total_k, Hkv, D], out [total_q, Hq, D],
  *   lse [Hq, total_q] float32.  cu_seqlens_q/k: device int32 [B+1] prefix sums;

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_append", "fa_combine",
+    assert {"fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_append", "fa_combine",
             "fa_kvcache_workspace_size", "fa_kvcache_num_splits", "fa_status_string",
             "fa_last_error"} <= set(names)
     for n in names:
@@ -145,6 +145,21 @@ def test_kvcache_append_rejects(lib):
     assert ap(S=0, Sq=0) == 0                 # nothing to do
     assert lib.fa_fwd_kvcache_append(1, None, None, None, None, None, 0, 0, 0, 0, None, None, 0, None, None,
                                      None, 0, None, None, 0, 1, 32, 8, 128, ob, None) == 0   # B = 0
+
+
+def test_fp8_rejects(lib):
+    ob, keep = _opts()
+
+    def f8(D=64, dq=1.0, dk=1.0, dv=1.0, B=1):
+        return lib.fa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, B, 8, 8, 2, 2, D, None, None, None, None,
+                              dq, dk, dv, ob, None)
+    assert f8(D=96) == 2                      # fp8: D 64 or 128
+    assert f8(D=256) == 2
+    assert f8(dq=0.0) == 1
+    assert f8(dk=-1.0) == 1
+    assert f8(dv=float("inf")) == 1
+    assert f8(dv=float("nan")) == 1
+    assert f8(B=0) == 0                       # no work
 
 
 def test_combine_rejects(lib):

@@ -539,3 +539,37 @@ def test_kvcache_append_then_decode_equals_prefilled_cache():
     torch.cuda.synchronize()
     assert torch.equal(kg, kg0) and torch.equal(vg, vg0)
     assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
+# ------------------------------------------------- fp8 e4m3 inputs
+
+FP8 = [
+    # (B, Sq, Sk, Hq, Hkv, D, descales (q, k, v), opts)
+    (2, 300, 300, 4, 2, 64, (1.0, 1.0, 1.0), dict(causal=True)),
+    (1, 257, 400, 4, 4, 64, (0.5, 2.0, 0.25), dict()),
+    (1, 200, 333, 4, 1, 128, (1.0, 1.0, 1.0), dict(causal=True)),
+    (2, 130, 130, 2, 2, 128, (0.125, 0.5, 2.0), dict(softcap=15.0, alibi=True, window=(40, 8))),
+    (1, 520, 520, 2, 2, 64, (1.0, 1.0, 1.0), dict(causal=True, window=(100, 0))),
+]
+
+
+@pytest.mark.parametrize("case", FP8, ids=lambda c: f"B{c[0]}q{c[1]}k{c[2]}d{c[5]}{sorted(c[7])}-{c[6]}")
+def test_fp8_prefill(case):
+    B, Sq, Sk, Hq, Hkv, D, (dq, dk, dv), opts = case
+    print("case fp8", case, flush=True)
+    q16, k16, v16 = inputs.dense_qkv(B, Sq, Sk, Hq, Hkv, D, torch.float32, seed=1700 + Sq + D)
+    # fp8 codes of values spread over e4m3's range; the descales give the real values
+    q8 = (q16 / dq).to(torch.float8_e4m3fn)
+    k8 = (k16 / dk).to(torch.float8_e4m3fn)
+    v8 = (v16 / dv).to(torch.float8_e4m3fn)
+    slopes = inputs.alibi_slopes(Hq) if opts.get("alibi") else None
+    kw = dict(causal=opts.get("causal", False), softcap=opts.get("softcap", 0.0))
+    out, lse = fa.fwd(q8.to(DEV), k8.to(DEV), v8.to(DEV), window_size=opts.get("window", (-1, -1)),
+                      alibi_slopes=None if slopes is None else slopes.to(DEV), q_descale=dq, k_descale=dk,
+                      v_descale=dv, **kw)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    deq = lambda t, s: (t.double() * s)
+    ro, rl = ref.attention(deq(q8, dq), deq(k8, dk), deq(v8, dv), window=opts.get("window", (-1, -1)),
+                           alibi_slopes=slopes, **kw)
+    check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"fp8 {case}")
