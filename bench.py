@@ -13,7 +13,8 @@ prefill kernel's mean duration from HIP events on the launch stream; the
 decode figure (GB/s of algorithmic K/V/q/out/block-table bytes over the
 decode + combine time) rides along in "decode".  "decode_append" times the
 same decode call with a one-token KV append per sequence (fwd_kvcache with
-k=, v=), after the timed steps.  "cpu_baseline" times the float64 CPU oracle
+k=, v=), and "prefill_fp8" the prefill on the same inputs converted to fp8
+e4m3, both after the timed steps.  "cpu_baseline" times the float64 CPU oracle
 on a bounded sample of the prefill workload.
 """
 
@@ -191,6 +192,24 @@ def main():
     d_bytes = decode_bytes(dc) if run_d else 0
     gbs = d_bytes / (d_mean * 1e-3) / 1e9
 
+    # the same prefill with q, k, v converted to fp8 e4m3 (descales 1)
+    f8_mean = None
+    if run_p:
+        q8, k8, v8 = (t.to(torch.float8_e4m3fn) for t in (q, k, v))
+        out8 = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup):
+            fa.fwd(q8, k8, v8, causal=True, out=out8, lse=lse)
+        torch.cuda.synchronize()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            fev[i][0].record()
+            fa.fwd(q8, k8, v8, causal=True, out=out8, lse=lse)
+            fev[i][1].record()
+        torch.cuda.synchronize()
+        f8_ms = [e[0].elapsed_time(e[1]) for e in fev]
+        f8_mean = sum(f8_ms) / len(f8_ms)
+        del q8, k8, v8, out8
+
     # decode with a one-token KV append (fwd_kvcache with k=, v=): every
     # sequence's last cached token is written again from k_new/v_new (its own
     # values, so the cache is unchanged) and then attended with the rest
@@ -265,6 +284,9 @@ def main():
                    "ms_min": round(min(d_ms), 5), "bytes": d_bytes, "dtype": "bf16",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": d_traffic}},
+        "prefill_fp8": None if f8_mean is None else {
+            "value": round(p_flops / (f8_mean * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_mean": round(f8_mean, 5),
+            "dtype": "fp8 e4m3 in (Q K^T on fp8 MFMA), bf16 P V and out"},
         "decode_append": None if a_mean is None else {
             "value": round(a_bytes / (a_mean * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_mean": round(a_mean, 5),
             "bytes": a_bytes, "new_tokens_per_sequence": 1,
