@@ -86,6 +86,15 @@ fa_status launch_status(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxGrid = 0x7fffffffLL;
 
+// compute units of the current device (256 if the query fails)
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,7 +134,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   if ((st = check_strides("q", qs, 3)) || (st = check_strides("k", ks, 3)) || (st = check_strides("v", vs, 3)) ||
       (st = check_strides("out", os, 3)))
     return st;
-  const int bm = fa::prefill_block_m(D);
+  const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, Sq, device_cus());
   const int64_t nqt = (Sq + bm - 1) / bm;
   if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
@@ -140,6 +149,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
+  p.block_m = bm;
   p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
   return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "prefill launch");
 }
@@ -187,6 +197,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
   fill_opts(p, opts, scale * q_descale * k_descale);   // scores of the dequantised q and k
   p.out_scale = v_descale;
   p.n_qtiles = (int)nqt;
+  p.block_m = bm;
   p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
   return launch_status(fa::launch_prefill_fp8(D, p, (hipStream_t)stream), "fp8 prefill launch");
 }
@@ -217,7 +228,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   if ((st = check_strides("q", qs, 2)) || (st = check_strides("k", ks, 2)) || (st = check_strides("v", vs, 2)) ||
       (st = check_strides("out", os, 2)))
     return st;
-  const int bm = fa::prefill_block_m(D);
+  const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, max_seqlen_q, device_cus());
   const int64_t nqt = (max_seqlen_q + bm - 1) / bm;
   if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
@@ -232,6 +243,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   p.B = B; p.Sq = max_seqlen_q; p.Sk = max_seqlen_k; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
+  p.block_m = bm;
   p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
   return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "varlen prefill launch");
 }

@@ -32,7 +32,8 @@ struct PrefillParams {
   const float* alibi;          // [Hq] slopes or nullptr
   int causal;
   int wl, wr;                  // window (left, right), -1 = unbounded
-  int n_qtiles;                // ceil(Sq / BLOCK_M)
+  int n_qtiles;                // ceil(Sq / block_m)
+  int block_m;                 // query rows per workgroup (prefill_block_m)
   int remap_xcd;               // 1 when the grid size is a multiple of 8
 };
 
@@ -112,6 +113,8 @@ hipError_t launch_append(const AppendParams& p, hipStream_t s);
 #define FA_PREFILL_RB128 1
 #endif
 // query rows per prefill workgroup for head dim D (the host sizes the grid with it)
-int prefill_block_m(int D);
+// query rows per prefill workgroup for B*Hq = heads and the longest query
+// sequence, on a device with cus compute units
+int prefill_block_m(int D, int64_t heads, int max_sq, int cus);
 
 }  // namespace fa

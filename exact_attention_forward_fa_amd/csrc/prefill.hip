@@ -415,50 +415,20 @@ void prefill_kernel(PrefillParams p) {
     }
   };
 
-  // ---- tile order: first the tiles whose every key is seen by every row of the
-  // workgroup (tf_lo .. tf_hi-1; no mask arithmetic, no per-tile liveness test,
-  // and no branch between the two products), then the tiles at the mask edges
-  // (t_lo .. tf_lo-1, then tf_hi .. t_hi-1).  The online softmax is exact in
-  // any tile order.
-  int tf_lo = t_lo, tf_hi = t_lo;
-  {
-    int f_lo = 0, f_hi = sk - 1;   // keys seen by every row of the workgroup
-    if (p.wl >= 0) f_lo = max(0, ip_last - p.wl);
-    if (p.causal) f_hi = min(f_hi, ip_first);
-    if (p.wr >= 0) f_hi = min(f_hi, ip_first + p.wr);
-    if (f_lo <= f_hi) {
-      const int a = (f_lo + BN - 1) / BN, z = (f_hi + 1) / BN;
-      if (a < z) { tf_lo = a; tf_hi = z; }
-    }
-  }
-  const int n_full = tf_hi - tf_lo, n_front = tf_lo - t_lo, n_all = t_hi - t_lo;
-  auto tile_at = [&](int i) __attribute__((always_inline)) {
-    const int e = i - n_full;
-    return i < n_full ? tf_lo + i : (e < n_front ? t_lo + e : tf_hi + e - n_front);
-  };
-  bool wave_live = false;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) wave_live |= m0 + rb * NW * 32 + wave * 32 < sq;
-
-  if (n_all > 0) {
-    gload(tile_at(0));
+  // ---- tiles in ascending key order.  Liveness and the need for masks are
+  // decided per wave from its own rows, so a wave's arithmetic does not depend
+  // on how many rows its workgroup holds.
+  if (t_lo < t_hi) {
+    gload(t_lo);
     swrite(0);
   }
   wait_vmem_all();   // Q operands ready: the loop waits only for its own tile loads
   __syncthreads();
 
-  int i = 0;
-  for (; i < n_full; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < n_all) gload(tile_at(i + 1));
-    if (wave_live) step(false, (tf_lo + i) * BN, ksm[buf], vsm[buf]);
-    if (i + 1 < n_all) swrite(buf ^ 1);
-    __syncthreads();
-  }
-  for (; i < n_all; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < n_all) gload(tile_at(i + 1));
-    const int j0 = tile_at(i) * BN;
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    if (t + 1 < t_hi) gload(t + 1);
+    const int j0 = t * BN;
     bool any_live = false, all_full = true;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -466,10 +436,8 @@ void prefill_kernel(PrefillParams p) {
       any_live |= live;
       all_full &= live && j0 >= lo_max[rb] && j0 + BN - 1 <= hi_min[rb];
     }
-    if (any_live) {
-      step(!all_full, j0, ksm[buf], vsm[buf]);
-    }
-    if (i + 1 < n_all) swrite(buf ^ 1);
+    if (any_live) step(!all_full, j0, ksm[buf], vsm[buf]);
+    if (t + 1 < t_hi) swrite(buf ^ 1);
     __syncthreads();
   }
 
@@ -776,22 +744,47 @@ template <> struct Shape<256> { static constexpr int NW = 4, RB = 1, BN = 32; };
 template <> struct Shape<64> { static constexpr int NW = FA_PREFILL_NW64, RB = FA_PREFILL_RB64, BN = 64; };
 template <> struct Shape<128> { static constexpr int NW = FA_PREFILL_NW128, RB = FA_PREFILL_RB128, BN = 64; };
 
-int prefill_block_m(int D) {
+// Query rows per workgroup.  The main kernel with 8 waves of 32 rows takes 256;
+// when B*Hq*ceil(Sq/256) workgroups would fill fewer than two per CU it drops
+// to 4 waves (128 rows) or 2 waves (64 rows), so more CUs get work (each wave
+// still owns 32 rows; the workgroups share K/V tiles among fewer waves).
+template <int D> static int block_m_of(int64_t heads, int max_sq, int cus) {
+  using S = Shape<D>;
   if (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128)) return 8 * 32;
-  if (D == 64) return Shape<64>::NW * 32 * Shape<64>::RB;
-  if (D == 128) return Shape<128>::NW * 32 * Shape<128>::RB;
-  if (D == 256) return Shape<256>::NW * 32 * Shape<256>::RB;
-  return 8 * 32;   // D = 32, 96
+  if (S::NW != 8 || S::RB != 1) return S::NW * 32 * S::RB;
+  auto wgs = [&](int bm) { return heads * ((max_sq + bm - 1) / bm); };
+  if (wgs(256) >= 2 * (int64_t)cus) return 256;
+  if (wgs(128) >= (int64_t)cus) return 128;
+  return 64;
+}
+
+int prefill_block_m(int D, int64_t heads, int max_sq, int cus) {
+  switch (D) {
+    case 32: return block_m_of<32>(heads, max_sq, cus);
+    case 64: return block_m_of<64>(heads, max_sq, cus);
+    case 96: return block_m_of<96>(heads, max_sq, cus);
+    case 256: return block_m_of<256>(heads, max_sq, cus);
+    default: return block_m_of<128>(heads, max_sq, cus);
+  }
 }
 
 template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
   using S = Shape<D>;
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
-  if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128))
+  if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128)) {
     hipLaunchKernelGGL((prefill_pp_kernel<E, D, 64, SC, AL>), dim3(grid), dim3(512), 0, s, p);
-  else
+  } else if constexpr (S::NW == 8 && S::RB == 1) {
+    // fewer rows per workgroup when the grid would leave CUs idle (see prefill_block_m)
+    if (p.block_m == 64)
+      hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, 2, 1, SC, AL>), dim3(grid), dim3(128), 0, s, p);
+    else if (p.block_m == 128)
+      hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, 4, 1, SC, AL>), dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, 8, 1, SC, AL>), dim3(grid), dim3(512), 0, s, p);
+  } else {
     hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, S::NW, S::RB, SC, AL>), dim3(grid), dim3(S::NW * 64), 0, s, p);
+  }
   return hipGetLastError();
 }
 
