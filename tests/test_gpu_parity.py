@@ -573,3 +573,19 @@ def test_fp8_prefill(case):
     ro, rl = ref.attention(deq(q8, dq), deq(k8, dk), deq(v8, dv), window=opts.get("window", (-1, -1)),
                            alibi_slopes=slopes, **kw)
     check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"fp8 {case}")
+
+
+@pytest.mark.parametrize("opts", [dict(causal=True), dict(window=(100, 20)), dict(causal=True, softcap=8.0)])
+def test_prefill_same_bits_for_any_workgroup_rows(opts):
+    """A small grid runs 64-row workgroups and a large one 256-row workgroups; each
+    wave owns the same 32 rows and walks the same tiles either way, so the
+    results of one (batch, head) agree bit for bit."""
+    q, k, v = inputs.dense_qkv(1, 512, 600, 2, 2, 64, torch.float16, seed=4711)
+    small = fa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=opts.get("causal", False),
+                   window_size=opts.get("window", (-1, -1)), softcap=opts.get("softcap", 0.0))
+    rep = lambda t: t.expand(128, -1, -1, -1).contiguous().to(DEV)
+    large = fa.fwd(rep(q), rep(k), rep(v), causal=opts.get("causal", False),
+                   window_size=opts.get("window", (-1, -1)), softcap=opts.get("softcap", 0.0))
+    torch.cuda.synchronize()
+    assert torch.equal(small[0][0], large[0][0]) and torch.equal(small[0][0], large[0][127])
+    assert torch.equal(small[1][0], large[1][0])
