@@ -110,15 +110,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   constexpr int VROW = D + 16;            // V LDS row stride (elements): conflict-free transposing reads
   constexpr int KROW = D + 8;             // K LDS row stride: conflict-free 16-byte reads
   constexpr int CH = D / 8;               // 16-byte pieces per K/V row
-  constexpr int NL = C * CH / 64;         // K (and V) pieces a lane loads per chunk, one per row
-  constexpr int RPI = 64 / CH;            // rows covered by one 16-byte load of all 64 lanes
+  // lanes per row: CH rounded up to a power of two (D = 96: 16 lanes for 12
+  // pieces; the other 4 reread piece 0 and store nothing)
+  constexpr int CHP = CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32;
+  constexpr int NL = C * CHP / 64;        // K (and V) pieces a lane loads per chunk, one per row
+  constexpr int RPI = 64 / CHP;           // rows covered by one 16-byte load of all 64 lanes
   constexpr int NE = MODE == 2 ? NL : 1;  // page numbers a lane holds per chunk
-  static_assert(NL * 64 == C * CH, "");
+  static_assert(NL * 64 == C * CHP, "");
   constexpr int NG = C / 16;              // 16-token groups per chunk (MFMA M blocks of S^T)
   __shared__ __attribute__((aligned(16))) T vbuf[C * VROW];
   __shared__ __attribute__((aligned(16))) T kbuf[C * KROW];
 
   const int lane = threadIdx.x, n = lane & 15, q4 = lane >> 4;
+  const int lpc = lane % CHP;             // this lane's piece of its row
+  const bool piece_ok = CH == CHP || lpc < CH;
+  const int lcol = piece_ok ? lpc : 0;    // the piece it loads
   const int P = gridDim.x, w = blockIdx.x;
   const int per_seq = p.num_splits * p.Hkv;
   const int n_items = p.B * per_seq;
@@ -224,19 +230,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       } else {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-          const int r = RPI * i + lane / CH;
+          const int r = RPI * i + lane / CHP;
           e[i] = bt[d.ok ? div_page(min(d.base + r, d.te - 1)) : 0];
         }
       }
     }
   };
-  // LDS tile: row RPI*i + lane/CH, 16-byte piece lane%CH, from one base address
-  // per lane and constant offsets
-  T* const kst = kbuf + (lane / CH) * KROW + (lane % CH) * 8;
-  T* const vst = vbuf + (lane / CH) * VROW + (lane % CH) * 8;
+  // LDS tile: row RPI*i + lane/CHP, 16-byte piece lane%CHP, from one base
+  // address per lane and constant offsets
+  T* const kst = kbuf + (lane / CHP) * KROW + lcol * 8;
+  T* const vst = vbuf + (lane / CHP) * VROW + lcol * 8;
   auto put = [&](int i, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) __attribute__((always_inline)) {
-    *(u32x4*)(kst + i * RPI * KROW) = kr[i];
-    *(u32x4*)(vst + i * RPI * VROW) = vr[i];
+    if (piece_ok) {
+      *(u32x4*)(kst + i * RPI * KROW) = kr[i];
+      *(u32x4*)(vst + i * RPI * VROW) = vr[i];
+    }
   };
 
   // Load chunk d: its K and V rows (rows past the item's end repeat its last
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       const char* kb8 = (const char*)p.k;
       const char* vb8 = (const char*)p.v;
       const uint32_t rowb = (uint32_t)(row_elems * sizeof(T));
-      const int lr = lane / CH, c = lane % CH;
+      const int lr = lane / CHP, c = lcol;
       const uint32_t lane_off = (uint32_t)hk * (uint32_t)(D * sizeof(T)) + (uint32_t)c * 16u;
       const int tl = d.te - 1;
       if constexpr (MODE == 2) {
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     } else {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int r = RPI * i + lane / CH, c = lane % CH;
+        const int r = RPI * i + lane / CHP, c = lcol;
         const int t = min(d.base + r, d.te - 1);
         int64_t row;
         if constexpr (MODE == 0) {
@@ -541,6 +549,7 @@ hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s) 
   switch (D) {
     case 32: return dt == kF16 ? launch_d<F16, 32>(p, cus, s) : launch_d<BF16, 32>(p, cus, s);
     case 64: return dt == kF16 ? launch_d<F16, 64>(p, cus, s) : launch_d<BF16, 64>(p, cus, s);
+    case 96: return dt == kF16 ? launch_d<F16, 96>(p, cus, s) : launch_d<BF16, 96>(p, cus, s);
     case 256: return dt == kF16 ? launch_d<F16, 256>(p, cus, s) : launch_d<BF16, 256>(p, cus, s);
     default: return dt == kF16 ? launch_d<F16, 128>(p, cus, s) : launch_d<BF16, 128>(p, cus, s);
   }

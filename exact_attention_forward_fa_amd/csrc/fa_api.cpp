@@ -48,16 +48,14 @@ fa_status check_opts(const fa_attn_opts* o, int D, float* scale_out) {
   return FA_OK;
 }
 
-// prefill: D in {32, 64, 96, 128, 256}; decode: D in {32, 64, 128, 256}
-fa_status check_common(int dtype, int Hq, int Hkv, int D, bool prefill) {
+// D in {32, 64, 96, 128, 256} for every call
+fa_status check_common(int dtype, int Hq, int Hkv, int D) {
   if (dtype != FA_F16 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
   if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
   if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "Hkv=%d must divide Hq=%d", Hkv, Hq);
   if (D <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "head_dim must be positive (D=%d)", D);
-  if (prefill && D != 32 && D != 64 && D != 96 && D != 128 && D != 256)
+  if (D != 32 && D != 64 && D != 96 && D != 128 && D != 256)
     return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built (32, 64, 96, 128 or 256)", D);
-  if (!prefill && D != 32 && D != 64 && D != 128 && D != 256)
-    return fail(FA_ERR_UNSUPPORTED, "head_dim %d not built for decode (32, 64, 128 or 256)", D);
   return FA_OK;
 }
 
@@ -116,7 +114,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
                  int B, int Sq, int Sk, int Hq, int Hkv, int D,
                  const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
                  const int64_t* o_stride, const fa_attn_opts* opts, void* stream) {
-  fa_status st = check_common(dtype, Hq, Hkv, D, true);
+  fa_status st = check_common(dtype, Hq, Hkv, D);
   if (st) return st;
   if (B < 0 || Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Sk=%d)", B, Sq, Sk);
   float scale;
@@ -159,7 +157,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
                      const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
                      const int64_t* o_stride, float q_descale, float k_descale, float v_descale,
                      const fa_attn_opts* opts, void* stream) {
-  fa_status st = check_common(FA_BF16, Hq, Hkv, D, true);
+  fa_status st = check_common(FA_BF16, Hq, Hkv, D);
   if (st) return st;
   if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "fp8 head_dim %d not built (64 or 128)", D);
   if (B < 0 || Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Sk=%d)", B, Sq, Sk);
@@ -208,7 +206,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
                         int Hq, int Hkv, int D,
                         const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
                         const int64_t* o_stride, const fa_attn_opts* opts, void* stream) {
-  fa_status st = check_common(dtype, Hq, Hkv, D, true);
+  fa_status st = check_common(dtype, Hq, Hkv, D);
   if (st) return st;
   if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
@@ -279,7 +277,7 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
                               int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream,
                               const void* k_new, const void* v_new, int S_new,
                               const int64_t* kn_stride, const int64_t* vn_stride) {
-  fa_status st = check_common(dtype, Hq, Hkv, D, false);
+  fa_status st = check_common(dtype, Hq, Hkv, D);
   if (st) return st;
   if (B < 0 || Sq < 0 || num_blocks_or_smax < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
   if (num_splits < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");

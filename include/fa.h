@@ -18,9 +18,9 @@
  *  - Element type: fa_dtype (fp16 or bf16) for q/k/v/out; float32 for lse,
  *    ALiBi slopes and the decode workspace; int32 for cu_seqlens,
  *    cache_seqlens and block_table.
- *  - Head dimension D: 32, 64, 96, 128 or 256 for fa_fwd / fa_fwd_varlen; 32, 64,
- *    128 or 256 for the KV-cache calls; any D for fa_combine.  Other values
- *    return FA_ERR_UNSUPPORTED.  The head-dim stride is 1 and row starts must be
+ *  - Head dimension D: 32, 64, 96, 128 or 256 for fa_fwd, fa_fwd_varlen and the
+ *    KV-cache calls; any D for fa_combine.  Other values return
+ *    FA_ERR_UNSUPPORTED.  The head-dim stride is 1 and row starts must be
  *    16-byte aligned (strides multiples of 8 elements, base pointers 16-byte
  *    aligned).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only

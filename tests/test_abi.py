@@ -121,7 +121,7 @@ def test_kvcache_workspace_and_rejects(lib):
     assert kv(Sq=5) == 2                      # 4 * 5 = 20 rows > 16
     assert kv(page=0) == 1
     assert lib.fa_fwd_kvcache(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 100, 16, FAKE, 1 << 30, FAKE, FAKE,
-                              4, 1, 32, 8, 96, ob, None) == 2   # head dim 96: prefill only
+                              4, 1, 32, 8, 80, ob, None) == 2   # head dim 80: not built
     assert kv(bts=0) == 1
 
 

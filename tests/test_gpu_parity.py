@@ -293,8 +293,10 @@ def test_paged_decode_options(page, Hq, Hkv, sq, D, dt, ns, opts):
 
 @pytest.mark.parametrize("D,dt,page,paged", [(32, torch.float16, 64, True), (32, torch.bfloat16, 0, False),
                                              (256, torch.bfloat16, 256, True), (256, torch.float16, 16, True),
-                                             (256, torch.bfloat16, 0, False)])
-def test_decode_head_dims_32_256(D, dt, page, paged):
+                                             (256, torch.bfloat16, 0, False), (96, torch.bfloat16, 64, True),
+                                             (96, torch.float16, 256, True), (96, torch.float16, 0, False),
+                                             (96, torch.bfloat16, 16, True)])
+def test_decode_head_dims_32_96_256(D, dt, page, paged):
     print("case decode D", D, dt, page, paged, flush=True)
     lens = [700, 33, 1500]
     pc = inputs.paged_cache(3, 2, 8, 2, D, dt, seed=900 + D + page, page_size=page or 64, lengths=lens,
@@ -469,6 +471,8 @@ APPEND = [
     (False, 0, 2, [17, 300], 6, 0, 4, 4, 64, torch.float16, False),       # Sq = 0: append only
     (True, 64, 2, [130, 70], 2, 2, 4, 2, 256, torch.bfloat16, True),
     (False, 0, 2, [40, 9], 3, 1, 4, 4, 32, torch.float16, False),
+    (True, 64, 2, [130, 70], 3, 3, 8, 2, 96, torch.bfloat16, True),
+    (False, 0, 2, [300, 65], 1, 1, 4, 1, 96, torch.float16, False),
 ]
 
 
