@@ -1,4 +1,4 @@
-"""numpy float64 oracle for the exact attention forward (TEST INFRASTRUCTURE ONLY).
+"""numpy float64 oracle for exact attention, forward and backward (TEST INFRASTRUCTURE ONLY).
 
 Only the test suite, the smoke check and the ``cpu_baseline`` leg of the
 benchmark may use this module; the product path never does.
@@ -37,6 +37,14 @@ Options, and where each is defined:
 
 Inputs may be any float dtype (float16/bfloat16 tensors are upcast exactly);
 all arithmetic is float64.
+
+The backward (``attention_backward``) is the gradient of that same definition
+with respect to q, k and v, written out step by step on the materialised score
+rows.  The pages name the method's backward only through its two properties:
+the attention weights are recomputed instead of stored (xhh.club tag page, the
+summaries on tiling and recomputation; the skill page's overview), and a
+deterministic mode exists (update notes, v2.4; "FlashAttention 常用接口简单介绍",
+§5.3).  Neither changes the mathematical gradient, which is what this computes.
 """
 
 from __future__ import annotations
@@ -291,6 +299,72 @@ def combine(out_partial, lse_partial):
     wn = np.where(live[..., None], w / np.where(live, tot, 1.0)[..., None], 0.0)
     out = (op * wn[..., None, :]).sum(axis=-1)
     return out, lse
+
+
+def _head_backward(qb, kb, vb, gb, s, scale, softcap):
+    """Steps 2-6 of ``attention_backward`` for one (batch, query head).
+
+    s: the final score rows [Sq, Sk] (-inf where masked); gb: dout rows.
+    Returns (dq [Sq, D], dk [Sk, D], dv [Sk, D]) of this query head.
+    """
+    P = np.zeros_like(s)                                                      # step 2
+    live = np.isfinite(s).any(axis=1)
+    if live.any():
+        sl = s[live]
+        e = np.exp(sl - sl.max(axis=1, keepdims=True))
+        P[live] = e / e.sum(axis=1, keepdims=True)
+    dv = P.T @ gb                                                             # step 3
+    dP = gb @ vb.T
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))                       # step 4
+    dU = dS                                                                   # step 5
+    if softcap > 0.0:
+        t = np.tanh(scale * (qb @ kb.T) / softcap)
+        dU = dU * (1.0 - t * t)
+    dU = dU * scale
+    return dU @ kb, dU.T @ qb, dv                                             # step 6
+
+
+def attention_backward(q, k, v, dout, softmax_scale=None, causal=False, window=(-1, -1), softcap=0.0,
+                       alibi_slopes=None):
+    """Gradients (dq, dk, dv) of the loss sum(out * dout) for the dense forward.
+
+    Shapes as in ``attention``: q, dout [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D].
+    Per (batch, query head), on the full score rows:
+      1. raw u = scale · Q Kᵀ, then the forward's score s (softcap, ALiBi, mask);
+      2. P = softmax of each row of s (rows with no allowed key: P = 0);
+      3. dV += Pᵀ dO and dP = dO Vᵀ;
+      4. dS = P ∘ (dP − rowsum(P ∘ dP)), the Jacobian of a softmax row applied
+         to dP (masked entries have P = 0 and get no gradient);
+      5. back through the score transform: ALiBi adds a constant (slope ·
+         distance), so it passes dS unchanged; softcap s = c·tanh(u / c) has
+         derivative 1 − tanh²(u / c); the scale gives a factor scale;
+      6. dQ = dU K and dK += dUᵀ Q, with dU the gradient at the raw product.
+    GQA: a kv head collects dk and dv from all query heads that read it.
+    Returns float64 dq [B, Sq, Hq, D], dk and dv [B, Sk, Hkv, D].
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if dout.shape != q.shape or k.shape != (B, Sk, Hkv, D) or v.shape != k.shape or Hq % Hkv != 0:
+        raise ValueError("shape mismatch")
+    group = Hq // Hkv
+    scale = resolve_scale(softmax_scale, D)
+    slopes = None if alibi_slopes is None else _f64(alibi_slopes).reshape(-1)
+    rows = np.arange(Sq)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // group
+            qb, kb, vb, gb = q[b, :, h, :], k[b, :, hk, :], v[b, :, hk, :], dout[b, :, h, :]
+            s = _head_scores(qb, kb, rows, Sq, Sk, scale, float(softcap),
+                             None if slopes is None else slopes[h], causal, window)     # step 1
+            dqh, dkh, dvh = _head_backward(qb, kb, vb, gb, s, scale, float(softcap))
+            dq[b, :, h, :] = dqh
+            dk[b, :, hk, :] += dkh
+            dv[b, :, hk, :] += dvh
+    return dq, dk, dv
 
 
 def flops(Sq: int, Sk: int, D: int, causal=False, window=(-1, -1)) -> int:
