@@ -9,6 +9,8 @@ and the current stream.  The calls mirror the interface described on
 * ``fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, ...)``   packed sequences
 * ``fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, ...)``
 * ``combine(out_partial, lse_partial)``
+* ``bwd(dout, q, k, v, out, lse, ...)`` -> (dq, dk, dv)    gradients of ``fwd``
+* ``attention(q, k, v, ...)``      -> out, differentiable (``fwd`` + ``bwd``)
 
 There is no fallback: if libfa.so is missing or a tensor is not on the GPU the
 call raises.
@@ -21,8 +23,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "kvcache_workspace_size",
-           "kvcache_num_splits", "library_path", "load_library", "FaError"]
+__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "bwd", "attention", "kvcache_workspace_size",
+           "kvcache_num_splits", "bwd_workspace_size", "library_path", "load_library", "FaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa.so")
@@ -74,6 +76,10 @@ def load_library():
     lib.fa_fwd_kvcache_append.restype = I
     lib.fa_combine.argtypes = [P, P, I, I, I, I, I, I64P, I64P, I, P, I64P, P, P]
     lib.fa_combine.restype = I
+    lib.fa_bwd_workspace_size.argtypes = [I, I, I]
+    lib.fa_bwd_workspace_size.restype = Z
+    lib.fa_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64P, I64P, I64P, I64P, I64P, OP, P, Z, P]
+    lib.fa_bwd.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -333,3 +339,72 @@ def combine(out_partial, lse_partial, out_dtype=None, out=None, lse=None):
                           _DTYPES[out.dtype], _ptr(out), _strides(out, (0, 1, 2)), _ptr(lse),
                           _stream(out_partial.device)))
     return out, lse
+
+
+def bwd_workspace_size(B: int, Sq: int, Hq: int) -> int:
+    """Bytes of device workspace ``bwd`` needs (the float32 row sums dout·out)."""
+    return int(load_library().fa_bwd_workspace_size(B, Sq, Hq))
+
+
+def bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0,
+        alibi_slopes=None, dq=None, dk=None, dv=None, workspace=None, deterministic=True):
+    """Gradients of ``fwd``: returns (dq [B,Sq,Hq,D], dk, dv [B,Sk,Hkv,D]) for the
+    gradient ``dout`` of ``out``.  ``out`` and ``lse`` are what ``fwd`` returned
+    for the same q, k, v and options.  D is 64 or 128.  The kernels are
+    deterministic (``deterministic`` is accepted for interface parity)."""
+    _need_gpu(dout, q, k, v, out, lse)
+    if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise ValueError("dout, q, k, v, out must share dtype float16 or bfloat16")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape or out.shape != q.shape \
+            or dout.shape != q.shape:
+        raise ValueError("expected q, out, dout [B,Sq,Hq,D] and k, v [B,Sk,Hkv,D]")
+    if any(t.stride(-1) != 1 for t in (dout, q, k, v, out)):
+        raise ValueError("head_dim must be contiguous")
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("batch / head_dim mismatch")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, Sq]")
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
+        if t is not None and (t.shape != shape or t.dtype != q.dtype or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous tensor like its input")
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dv is None else dv
+    lib = load_library()
+    need = int(lib.fa_bwd_workspace_size(B, Sq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    _check(lib.fa_bwd(_DTYPES[q.dtype], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                      _ptr(dq), _ptr(dk), _ptr(dv), B, Sq, Sk, Hq, Hkv, D,
+                      _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)), _strides(v, (0, 1, 2)),
+                      _strides(out, (0, 1, 2)), _strides(dout, (0, 1, 2)), ob,
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, softmax_scale, causal, window_size, softcap, alibi_slopes):
+        out, lse = fwd(q, k, v, softmax_scale=softmax_scale, causal=causal, window_size=window_size,
+                       softcap=softcap, alibi_slopes=alibi_slopes)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.opts = (softmax_scale, causal, window_size, softcap, alibi_slopes)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        softmax_scale, causal, window_size, softcap, alibi_slopes = ctx.opts
+        dq, dk, dv = bwd(dout.contiguous(), q, k, v, out, lse, softmax_scale=softmax_scale, causal=causal,
+                         window_size=window_size, softcap=softcap, alibi_slopes=alibi_slopes)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def attention(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None):
+    """Differentiable dense attention: ``fwd`` forward, ``bwd`` backward (weights
+    recomputed from the saved lse).  Returns out [B, Sq, Hq, D]."""
+    return _Attention.apply(q, k, v, softmax_scale, causal, tuple(window_size), softcap, alibi_slopes)

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["prefill.hip", "decode.hip", "combine.hip", "append.hip", "fa_api.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "combine.hip", "append.hip", "backward.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are turned off for all device code.  The kernels

@@ -1,0 +1,554 @@
+// Backward kernels for gfx950: gradients of exact attention with respect to q,
+// k and v, with the attention weights recomputed from q, k and the forward's
+// log-sum-exp instead of being stored (xhh.club "flash attention" tag page, the
+// summaries on recomputation in the backward pass; the skill page's overview of
+// tiling plus recomputation).  Every result is produced by one workgroup in a
+// fixed order, so repeated calls give identical bits (the deterministic mode of
+// the Flash-Attention update notes, v2.4, and "FlashAttention 常用接口简单介绍",
+// §5.3, here the only mode).
+//
+// Per (query row i, key j) of one head, with s the forward's final score in
+// log2 units and L_i = lse_i·log2(e):
+//   P = 2^(s - L_i),  dV_j += P dO_i,  dP = dO_i · V_j,
+//   dS = P (dP - delta_i) with delta_i = dO_i · O_i (the row sum of P dP),
+//   dU = dS (1 - t²) under softcap (t = tanh of the capped argument), else dS,
+//   dQ_i += scale dU K_j,  dK_j += scale dU Q_i.
+//
+// Three kernels:
+//  * bwd_delta_kernel: delta_i = dO_i · O_i (fp32), one row per D/8 lanes.
+//  * bwd_dkdv_kernel: one workgroup per (key tile, kv head, batch); each wave
+//    owns 32 keys, keeps their K and V rows in registers and their dK and dV
+//    accumulators in registers, and streams the query tiles of every query head
+//    of its group through LDS.  S = Q Kᵀ and dP = dO Vᵀ put the key on the lane
+//    (column) side, so P and dS are already in the A-operand layout of
+//    dV += Pᵀ dO and dK += dSᵀ Q; dO and Q come out of LDS with the transposing
+//    read ds_read_b64_tr_b16.
+//  * bwd_dq_kernel: one workgroup per (query tile, query head, batch); each wave
+//    owns 32 queries, keeps their Q and dO rows in registers, and streams K and V
+//    tiles through LDS.  Sᵀ = K Qᵀ and dPᵀ = V dOᵀ put the query on the lane
+//    side, so dS is in the A-operand layout of dQ += dS K, with K read
+//    transposed.
+// Both streaming kernels hold their LDS tiles in an XOR-swizzled row-major
+// layout (swz below) that serves the plain 16-byte operand reads and the
+// transposing reads without bank conflicts.
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// Element offset of 16-byte chunk c of row r in a [rows, D] LDS tile.  The chunk
+// index is XORed with a function of the row such that
+//  * 16 consecutive rows read at one chunk index land on 16 distinct 16-byte
+//    bank groups (plain operand reads: lane <-> row), and
+//  * rows 4a .. 4a+3 read at the four chunks of one 64-byte column block land on
+//    four distinct 64-byte bank ranges (transposing reads).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  static_assert(D == 64 || D == 128, "");
+  if constexpr (D == 128) return r * D + 8 * (c ^ (4 * (r & 3) + ((r >> 2) & 3)));
+  else return r * D + 8 * (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
+}
+
+// ---------------------------------------------------------------------------
+// delta_i = sum_d dO[i, d] * O[i, d]
+// ---------------------------------------------------------------------------
+template <class E, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
+  using T = typename E::T;
+  using V8 = typename E::V8;
+  constexpr int CH = D / 8, RPB = 256 / CH;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CH;   // (b, i, h), h fastest
+  const int c = threadIdx.x % CH;
+  const int64_t nrows = (int64_t)p.B * p.Sq * p.Hq;
+  float acc = 0.f;
+  int64_t b = 0, i = 0, h = 0;
+  if (row < nrows) {
+    h = row % p.Hq;
+    const int64_t bi = row / p.Hq;
+    i = bi % p.Sq;
+    b = bi / p.Sq;
+    const V8 x = *(const V8*)((const T*)p.out + b * p.o_sb + i * p.o_ss + h * p.o_sh + c * 8);
+    const V8 y = *(const V8*)((const T*)p.dout + b * p.do_sb + i * p.do_ss + h * p.do_sh + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+  }
+#pragma unroll
+  for (int m = CH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < nrows && c == 0) p.delta[(b * p.Hq + h) * p.Sq + i] = acc;
+}
+
+// Score of one (query, key) pair in log2 units from the raw product x = q·k, and
+// the factor 1 - t² that softcap puts on the gradient (1 without softcap).
+template <bool SOFTCAP, bool ALIBI>
+__device__ __forceinline__ float score_l2(float x, float dist, float sl2, float cap_in, float cap_l2, float slope_l2,
+                                          float& dcap) {
+  float s;
+  if constexpr (SOFTCAP) {
+    const float e = exp2_fast(x * cap_in);                 // e^(2u/c), u = scale·x
+    const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+    s = cap_l2 * t;
+    dcap = 1.f - t * t;
+  } else {
+    s = x * sl2;
+    dcap = 1.f;
+  }
+  if constexpr (ALIBI) s = fmaf(-slope_l2, fabsf(dist), s);
+  return s;
+}
+
+constexpr int kBig = 1 << 30;
+
+// ---------------------------------------------------------------------------
+// dK, dV: workgroup = NW waves x 32 keys; query tiles of 64 rows through LDS
+// ---------------------------------------------------------------------------
+template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2)))
+void bwd_dkdv_kernel(BackwardParams p) {
+  using T = typename E::T;
+  using V8 = typename E::V8;
+  using V2 = typename E::V2;
+  constexpr int BMQ = 64;                 // query rows per LDS tile
+  constexpr int BNK = NW * 32;            // keys per workgroup
+  constexpr int CH = D / 8, DC = D / 16, DB = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int LQ = BMQ * CH / NT;       // 16-byte pieces per thread per tile, for Q and for dO
+  static_assert(LQ * NT == BMQ * CH, "");
+  __shared__ __attribute__((aligned(16))) T qsm[2][BMQ * D];
+  __shared__ __attribute__((aligned(16))) T gsm[2][BMQ * D];     // dO
+  __shared__ __attribute__((aligned(16))) float lsm[2][BMQ];     // lse in log2 units; +inf: row adds nothing
+  __shared__ __attribute__((aligned(16))) float esm[2][BMQ];     // delta
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // workgroup -> (batch, kv head, key tile); the heads are spread over the XCDs
+  // in contiguous ranges, and within a head the first key tiles (seen by the
+  // most queries under a causal mask) go first
+  int id = blockIdx.x;
+  if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
+  const int head = id / p.n_ktiles;
+  const int kt = id - head * p.n_ktiles;
+  const int b = head / p.Hkv, hk = head - b * p.Hkv;
+  const int sq = p.Sq, sk = p.Sk, shift = sk - sq;
+  const int n0 = kt * BNK;
+
+  // the lane's key and the query rows that may attend it: i in [a_j, b_j]
+  const int j = n0 + wave * 32 + l32;
+  const bool key_ok = j < sk;
+  const int jc = min(j, sk - 1);
+  int R = kBig;                            // key j allowed iff j <= i' + R (i' = i + shift) ...
+  if (p.causal) R = 0;
+  if (p.wr >= 0) R = min(R, p.wr);
+  const int Lw = p.wl >= 0 ? p.wl : kBig;  // ... and j >= i' - Lw
+  const int a_j = R == kBig ? 0 : max(0, j - shift - R);
+  const int b_j = Lw == kBig ? sq - 1 : min(sq - 1, j - shift + Lw);
+  // query range of the whole workgroup
+  const int qlo = R == kBig ? 0 : max(0, n0 - shift - R);
+  const int qhi = Lw == kBig ? sq : min(sq, min(n0 + BNK, sk) - 1 - shift + Lw + 1);
+  const int t_lo = qlo / BMQ;
+  const int nt = qhi > qlo ? (qhi + BMQ - 1) / BMQ - t_lo : 0;
+  const int total = nt * p.group;
+
+  // K and V rows of the lane's key: B operands of S = Q Kᵀ and dP = dO Vᵀ
+  // (lane <-> key, d = 16dc + 8hi .. +7)
+  V8 kr[DC], vr[DC];
+  {
+    const T* kp = (const T*)p.k + (int64_t)b * p.k_sb + (int64_t)jc * p.k_ss + (int64_t)hk * p.k_sh + hi * 8;
+    const T* vp = (const T*)p.v + (int64_t)b * p.v_sb + (int64_t)jc * p.v_ss + (int64_t)hk * p.v_sh + hi * 8;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      kr[dc] = *(const V8*)(kp + dc * 16);
+      vr[dc] = *(const V8*)(vp + dc * 16);
+    }
+  }
+  const float sl2 = p.scale * kLog2e;
+  const float cap_l2 = p.softcap * kLog2e;
+  const float cap_in = 2.f * p.scale * kLog2e / (SOFTCAP ? p.softcap : 1.f);
+
+  // ---- global -> registers -> LDS staging of query tile `it` (rows past sq are
+  // clamped to a real row and get lse = +inf, so their P is 0)
+  u32x4 qst[LQ], gst[LQ];
+  float lst = 0.f, est = 0.f;
+  auto gload = [&](int it) __attribute__((always_inline)) {
+    const int g = it / nt, t = t_lo + (it - g * nt);
+    const int hq = hk * p.group + g;
+    const int r0 = t * BMQ;
+    const T* qp = (const T*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
+    const T* gp = (const T*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh;
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+      const int row = min(r0 + r, sq - 1);
+      qst[i] = *(const u32x4*)(qp + (int64_t)row * p.q_ss + c * 8);
+      gst[i] = *(const u32x4*)(gp + (int64_t)row * p.do_ss + c * 8);
+    }
+    if (tid < BMQ) {
+      const int row = r0 + tid;
+      const int rc = min(row, sq - 1);
+      const float l = p.lse[(int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + rc];
+      const float d = p.delta[((int64_t)b * p.Hq + hq) * sq + rc];
+      lst = (row < sq && l != kNegInf) ? l * kLog2e : __builtin_inff();
+      est = row < sq ? d : 0.f;
+    }
+  };
+  auto swrite = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+      *(u32x4*)(&qsm[buf][swz<D>(r, c)]) = qst[i];
+      *(u32x4*)(&gsm[buf][swz<D>(r, c)]) = gst[i];
+    }
+    if (tid < BMQ) {
+      lsm[buf][tid] = lst;
+      esm[buf][tid] = est;
+    }
+  };
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  // transposing-read addressing: lane (4a + g) of each 16-lane group reads row
+  // 4hi + a (+8) of a 16-row chunk, elements 32db + 16((lane >> 4) & 1) + 4g .. +3
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_elem = 4 * (lane & 1);
+
+  // one block of 32 queries (rows rb0 .. rb0+31 of the tile, first row i0) against
+  // the wave's 32 keys
+  auto block = [&](const T* qs, const T* gs, const float* ls, const float* es, int rb0, int i0, bool edge,
+                   float slope_l2) __attribute__((always_inline)) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const int off = swz<D>(rb0 + l32, 2 * dc + hi);
+      s = E::mfma32(*(const V8*)(qs + off), kr[dc], s);
+      dp = E::mfma32(*(const V8*)(gs + off), vr[dc], dp);
+    }
+    // register r of s holds query row rb0 + 8(r/4) + 4hi + r%4 for the lane's key
+    f32x4 L[4], Dl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      L[t] = *(const f32x4*)(ls + rb0 + 8 * t + 4 * hi);
+      Dl[t] = *(const f32x4*)(es + rb0 + 8 * t + 4 * hi);
+    }
+    V8 pa[2], sa[2];
+    const float dist0 = (float)(i0 + 4 * hi + shift - j);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float pr[2], ds[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rr = r + u;
+        const int qo = 8 * (rr >> 2) + (rr & 3);
+        float dcap;
+        const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 + (float)qo, sl2, cap_in, cap_l2, slope_l2, dcap);
+        float pv = exp2_fast(x - L[rr >> 2][rr & 3]);
+        if (edge) {
+          const int i = i0 + 4 * hi + qo;
+          if (i < a_j || i > b_j) pv = 0.f;
+        }
+        pr[u] = pv;
+        ds[u] = pv * (dp[rr] - Dl[rr >> 2][rr & 3]) * dcap;
+      }
+      const V2 pp = E::pack(pr[0], pr[1]);
+      const V2 sp = E::pack(ds[0], ds[1]);
+      pa[r >> 3][r & 7] = pp[0];
+      pa[r >> 3][(r & 7) + 1] = pp[1];
+      sa[r >> 3][r & 7] = sp[0];
+      sa[r >> 3][(r & 7) + 1] = sp[1];
+    }
+    // dV += Pᵀ dO and dK += dSᵀ Q over two 16-query chunks; the contraction order
+    // inside a chunk is the register order of P, matched by the transposing read
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int r1 = rb0 + 16 * c2 + tr_row, r2 = r1 + 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int o1 = swz<D>(r1, 4 * db + tr_chunk) + tr_elem;
+        const int o2 = swz<D>(r2, 4 * db + tr_chunk) + tr_elem;
+        const i16x4 g0 = lds_read_tr16(gs + o1), g1 = lds_read_tr16(gs + o2);
+        const i16x4 q0 = lds_read_tr16(qs + o1), q1 = lds_read_tr16(qs + o2);
+        const V8 gb = __builtin_bit_cast(V8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const V8 qb = __builtin_bit_cast(V8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+        dv[db] = E::mfma32(pa[c2], gb, dv[db]);
+        dk[db] = E::mfma32(sa[c2], qb, dk[db]);
+      }
+    }
+  };
+
+  if (total > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < total) gload(it + 1);
+    const int g = it / nt, t = t_lo + (it - g * nt);
+    const int hq = hk * p.group + g;
+    const float slope_l2 = ALIBI ? p.alibi[hq] * kLog2e : 0.f;
+#pragma unroll
+    for (int blk = 0; blk < BMQ / 32; ++blk) {
+      const int i0 = t * BMQ + blk * 32;
+      const bool live = key_ok && max(a_j, i0) <= min(b_j, i0 + 31);
+      if (!__any(live)) continue;
+      const bool full = !key_ok || (a_j <= i0 && b_j >= i0 + 31);
+      block(qsm[buf], gsm[buf], lsm[buf], esm[buf], blk * 32, i0, !__all(full), slope_l2);
+    }
+    if (it + 1 < total) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: register r of dk[db] / dv[db] is key n0 + 32w + 8(r/4) + 4hi + r%4,
+  // column d = 32db + l32
+  T* dkp = (T*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hk * p.dk_sh;
+  T* dvp = (T*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hk * p.dv_sh;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = n0 + wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (key < sk) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dkp[(int64_t)key * p.dk_ss + db * 32 + l32] = E::from_f32(dk[db][r] * p.scale);
+        dvp[(int64_t)key * p.dv_ss + db * 32 + l32] = E::from_f32(dv[db][r]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: workgroup = NW waves x 32 queries; key tiles of 64 rows through LDS
+// ---------------------------------------------------------------------------
+template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(BackwardParams p) {
+  using T = typename E::T;
+  using V8 = typename E::V8;
+  using V2 = typename E::V2;
+  constexpr int BN = 64;                  // keys per LDS tile
+  constexpr int BM = NW * 32;             // queries per workgroup
+  constexpr int CH = D / 8, DC = D / 16, DB = D / 32;
+  constexpr int NT = NW * 64;
+  constexpr int LK = BN * CH / NT;
+  static_assert(LK * NT == BN * CH, "");
+  __shared__ __attribute__((aligned(16))) T ksm[2][BN * D];
+  __shared__ __attribute__((aligned(16))) T vsm[2][BN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int id = blockIdx.x;
+  if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
+  const int head = id / p.n_qtiles;
+  const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);   // last (longest) query tiles first
+  const int b = head / p.Hq, hq = head - b * p.Hq;
+  const int hk = hq / p.group;
+  const int sq = p.Sq, sk = p.Sk, shift = sk - sq;
+  const int m0 = qt * BM;
+
+  // the lane's query row and its allowed keys [j_lo, j_hi]
+  const int i = m0 + wave * 32 + l32;
+  const bool row_ok = i < sq;
+  const int ic = min(i, sq - 1);
+  const int ip = i + shift;
+  int j_lo = 0, j_hi = sk - 1;
+  if (p.wl >= 0) j_lo = max(j_lo, ip - p.wl);
+  if (p.causal) j_hi = min(j_hi, ip);
+  if (p.wr >= 0) j_hi = min(j_hi, ip + p.wr);
+  // key range of the workgroup
+  const int ip_first = m0 + shift, ip_last = min(m0 + BM, sq) - 1 + shift;
+  int kv_lo = 0, kv_hi = sk;
+  if (p.wl >= 0) kv_lo = max(0, ip_first - p.wl);
+  if (p.causal) kv_hi = min(kv_hi, ip_last + 1);
+  if (p.wr >= 0) kv_hi = min(kv_hi, ip_last + p.wr + 1);
+  const int t_lo = kv_lo / BN;
+  const int t_hi = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : t_lo;
+
+  // Q and dO rows of the lane's query: B operands of Sᵀ = K Qᵀ and dPᵀ = V dOᵀ
+  V8 qr[DC], gr[DC];
+  {
+    const T* qp = (const T*)p.q + (int64_t)b * p.q_sb + (int64_t)ic * p.q_ss + (int64_t)hq * p.q_sh + hi * 8;
+    const T* gp = (const T*)p.dout + (int64_t)b * p.do_sb + (int64_t)ic * p.do_ss + (int64_t)hq * p.do_sh + hi * 8;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      qr[dc] = *(const V8*)(qp + dc * 16);
+      gr[dc] = *(const V8*)(gp + dc * 16);
+    }
+  }
+  const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + ic];
+  const float L = (row_ok && lse != kNegInf) ? lse * kLog2e : __builtin_inff();
+  const float Dl = row_ok ? p.delta[((int64_t)b * p.Hq + hq) * sq + ic] : 0.f;
+  const float sl2 = p.scale * kLog2e;
+  const float cap_l2 = p.softcap * kLog2e;
+  const float cap_in = 2.f * p.scale * kLog2e / (SOFTCAP ? p.softcap : 1.f);
+  const float slope_l2 = ALIBI ? p.alibi[hq] * kLog2e : 0.f;
+
+  const T* kp = (const T*)p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
+  const T* vp = (const T*)p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+  u32x4 kst[LK], vst[LK];
+  auto gload = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LK; ++u) {
+      const int cid = tid + u * NT, r = cid / CH, c = cid - r * CH;
+      const int row = min(t * BN + r, sk - 1);
+      kst[u] = *(const u32x4*)(kp + (int64_t)row * p.k_ss + c * 8);
+      vst[u] = *(const u32x4*)(vp + (int64_t)row * p.v_ss + c * 8);
+    }
+  };
+  auto swrite = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LK; ++u) {
+      const int cid = tid + u * NT, r = cid / CH, c = cid - r * CH;
+      *(u32x4*)(&ksm[buf][swz<D>(r, c)]) = kst[u];
+      *(u32x4*)(&vsm[buf][swz<D>(r, c)]) = vst[u];
+    }
+  };
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_elem = 4 * (lane & 1);
+
+  // keys kb0 .. kb0+31 of the tile (first key j0) against the wave's 32 queries
+  auto block = [&](const T* ks, const T* vs, int kb0, int j0, bool edge) __attribute__((always_inline)) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const int off = swz<D>(kb0 + l32, 2 * dc + hi);
+      s = E::mfma32(*(const V8*)(ks + off), qr[dc], s);
+      dp = E::mfma32(*(const V8*)(vs + off), gr[dc], dp);
+    }
+    // register r holds key j0 + 8(r/4) + 4hi + r%4 for the lane's query
+    V8 sa[2];
+    const float dist0 = (float)(ip - j0 - 4 * hi);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float ds[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rr = r + u;
+        const int ko = 8 * (rr >> 2) + (rr & 3);
+        float dcap;
+        const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 - (float)ko, sl2, cap_in, cap_l2, slope_l2, dcap);
+        float pv = exp2_fast(x - L);
+        if (edge) {
+          const int jj = j0 + 4 * hi + ko;
+          if (jj < j_lo || jj > j_hi) pv = 0.f;
+        }
+        ds[u] = pv * (dp[rr] - Dl) * dcap;
+      }
+      const V2 sp = E::pack(ds[0], ds[1]);
+      sa[r >> 3][r & 7] = sp[0];
+      sa[r >> 3][(r & 7) + 1] = sp[1];
+    }
+    // dQ += dS K over two 16-key chunks, K read transposed
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int r1 = kb0 + 16 * c2 + tr_row, r2 = r1 + 8;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 k0 = lds_read_tr16(ks + swz<D>(r1, 4 * db + tr_chunk) + tr_elem);
+        const i16x4 k1 = lds_read_tr16(ks + swz<D>(r2, 4 * db + tr_chunk) + tr_elem);
+        const V8 kb = __builtin_bit_cast(V8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+        dq[db] = E::mfma32(sa[c2], kb, dq[db]);
+      }
+    }
+  };
+
+  if (t_hi > t_lo) {
+    gload(t_lo);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int buf = (t - t_lo) & 1;
+    if (t + 1 < t_hi) gload(t + 1);
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      const int j0 = t * BN + kb * 32;
+      const bool live = row_ok && max(j_lo, j0) <= min(j_hi, j0 + 31);
+      if (!__any(live)) continue;
+      const bool full = !row_ok || (j_lo <= j0 && j_hi >= j0 + 31);
+      block(ksm[buf], vsm[buf], kb * 32, j0, !__all(full));
+    }
+    if (t + 1 < t_hi) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: register r of dq[db] is query m0 + 32w + 8(r/4) + 4hi + r%4, d = 32db + l32
+  T* dqp = (T*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+    if (row < sq) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dqp[(int64_t)row * p.dq_ss + db * 32 + l32] = E::from_f32(dq[db][r] * p.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <int D> constexpr int bwd_dkdv_waves() { return D >= 128 ? 4 : 8; }
+constexpr int kBwdDqWaves = 8;
+
+int backward_block_n(int D) { return (D >= 128 ? 4 : 8) * 32; }
+int backward_block_m(int) { return kBwdDqWaves * 32; }
+
+template <class E, int D, bool SOFTCAP, bool ALIBI>
+hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
+  constexpr int NWK = bwd_dkdv_waves<D>();
+  const int64_t gk = (int64_t)p.n_ktiles * p.B * p.Hkv;
+  if (gk > 0) {
+    BackwardParams pk = p;
+    pk.remap_xcd = gk % 8 == 0;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t gq = (int64_t)p.n_qtiles * p.B * p.Hq;
+  if (gq > 0) {
+    BackwardParams pq = p;
+    pq.remap_xcd = gq % 8 == 0;
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, kBwdDqWaves, SOFTCAP, ALIBI>), dim3((unsigned)gq), dim3(kBwdDqWaves * 64),
+                       0, s, pq);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <class E, int D>
+hipError_t launch_bwd_d(const BackwardParams& p, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_delta_kernel<E, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const bool cap = p.softcap > 0.f, al = p.alibi != nullptr;
+  if (cap && al) return launch_bwd_main<E, D, true, true>(p, s);
+  if (cap) return launch_bwd_main<E, D, true, false>(p, s);
+  if (al) return launch_bwd_main<E, D, false, true>(p, s);
+  return launch_bwd_main<E, D, false, false>(p, s);
+}
+
+template <class E>
+hipError_t launch_bwd_e(int D, const BackwardParams& p, hipStream_t s) {
+  if (D == 64) return launch_bwd_d<E, 64>(p, s);
+  return launch_bwd_d<E, 128>(p, s);
+}
+
+hipError_t launch_backward(Dtype dt, int D, const BackwardParams& p, hipStream_t s) {
+  if (dt == kBF16) return launch_bwd_e<BF16>(D, p, s);
+  return launch_bwd_e<F16>(D, p, s);
+}
+
+}  // namespace fa

@@ -91,6 +91,39 @@ struct CombineParams {
   int B, S, H, D, num_splits;
 };
 
+// Backward (gradients of q, k, v) of the dense forward, weights recomputed from lse.
+struct BackwardParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;            // [B, Hq, Sq] as written by the forward
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;                // workspace [B, Hq, Sq]: rowsum(dout * out)
+  // element strides: batch, sequence, head (head_dim stride is 1)
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t dq_sb, dq_ss, dq_sh;
+  int64_t dk_sb, dk_ss, dk_sh;
+  int64_t dv_sb, dv_ss, dv_sh;
+  int64_t lse_sb, lse_sh;
+  int B, Sq, Sk, Hq, Hkv, group;
+  float scale;
+  float softcap;
+  const float* alibi;
+  int causal;
+  int wl, wr;
+  int n_ktiles;                // ceil(Sk / backward_block_n(D))
+  int n_qtiles;                // ceil(Sq / backward_block_m(D))
+  int remap_xcd;               // set per kernel by the launcher
+};
+
 hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s);
 // fp8 e4m3 q/k/v, bf16 out; D in {64, 128}
 hipError_t launch_prefill_fp8(int D, const PrefillParams& p, hipStream_t s);
@@ -98,6 +131,10 @@ int prefill_block_m_fp8(int D);
 hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s);
 hipError_t launch_combine(Dtype dt, const CombineParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+// D in {64, 128}; launches nothing for an empty grid
+hipError_t launch_backward(Dtype dt, int D, const BackwardParams& p, hipStream_t s);
+int backward_block_n(int D);   // keys per dK/dV workgroup
+int backward_block_m(int D);   // queries per dQ workgroup
 
 // Prefill workgroup shape per head dim: NW waves, each owning RB blocks of 32 query rows.
 #ifndef FA_PREFILL_NW64

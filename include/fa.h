@@ -192,6 +192,37 @@ fa_status fa_combine(const float* out_partial, const float* lse_partial, int B, 
                      int num_splits, const int64_t* op_stride, const int64_t* lp_stride,
                      fa_dtype out_dtype, void* out, const int64_t* o_stride, float* lse, void* stream);
 
+/* Bytes of workspace fa_bwd needs: the float32 row sums delta [B, Hq, Sq]
+ * (delta_i = dout_i · out_i), padded to 256 bytes; 0 when B, Sq or Hq is 0. */
+size_t fa_bwd_workspace_size(int B, int Sq, int Hq);
+
+/*
+ * Backward of fa_fwd: gradients of a loss with respect to q, k and v given its
+ * gradient dout with respect to out.  The attention weights are recomputed from
+ * q, k and the forward's lse rather than stored (xhh.club "flash attention" tag
+ * page, the summaries on recomputation in the backward pass); every output
+ * element is written by one workgroup in a fixed order, so repeated calls give
+ * identical bits (the deterministic backward of the update notes, v2.4, and
+ * "FlashAttention 常用接口简单介绍", §5.3).
+ *   dout, q, out [B, Sq, Hq, D] and k, v [B, Sk, Hkv, D] (dtype) with element
+ *   strides as in fa_fwd (do_stride for dout; NULL = contiguous); lse
+ *   [B, Hq, Sq] float32 as written by fa_fwd for the same inputs and options.
+ *   dq [B, Sq, Hq, D], dk and dv [B, Sk, Hkv, D] (dtype), contiguous, are
+ *   overwritten; GQA kv heads receive the sum over their query heads.  Keys no
+ *   query may attend get dk = dv = 0, rows with no allowed key get dq = 0.
+ *   opts must be those of the forward call.  D is 64 or 128.
+ *   workspace: device memory of at least fa_bwd_workspace_size(B, Sq, Hq)
+ *   bytes, 16-byte aligned, owned by the caller (NULL allowed when that is 0);
+ *   FA_ERR_WORKSPACE_TOO_SMALL otherwise.  Arithmetic: products in fp32 from
+ *   the fp16/bf16 inputs; P and dS are rounded to the input dtype before the
+ *   products that accumulate dv, dk and dq in fp32.
+ */
+fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k, const void* v, const void* out,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                 const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                 const int64_t* o_stride, const int64_t* do_stride, const fa_attn_opts* opts,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(fa_status status);
 /* Detail of the last error returned on the calling thread ("" if none). */

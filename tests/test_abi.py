@@ -28,8 +28,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_append", "fa_combine",
-            "fa_kvcache_workspace_size", "fa_kvcache_num_splits", "fa_status_string",
-            "fa_last_error"} <= set(names)
+            "fa_kvcache_workspace_size", "fa_kvcache_num_splits", "fa_bwd", "fa_bwd_workspace_size",
+            "fa_status_string", "fa_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} missing from libfa.so"
 
@@ -160,6 +160,46 @@ def test_fp8_rejects(lib):
     assert f8(dv=float("inf")) == 1
     assert f8(dv=float("nan")) == 1
     assert f8(B=0) == 0                       # no work
+
+
+def test_bwd_workspace_size(lib):
+    assert lib.fa_bwd_workspace_size(4, 4096, 32) == 4 * 32 * 4096 * 4
+    assert lib.fa_bwd_workspace_size(1, 3, 5) == 256           # 60 bytes padded to 256
+    assert lib.fa_bwd_workspace_size(0, 8, 8) == 0
+    assert lib.fa_bwd_workspace_size(2, 0, 8) == 0
+
+
+def test_bwd_rejects(lib):
+    """Every argument error of the backward is reported before any launch."""
+    ob, keep = _opts()
+    WS = ctypes.c_void_p(1 << 21)
+
+    def bw(dtype=0, B=1, Sq=8, Sk=8, Hq=2, Hkv=2, D=64, ws=WS, wsb=1 << 20, ptrs=None, strides=None, o=None):
+        p = ptrs or [FAKE] * 9          # dout, q, k, v, out, lse, dq, dk, dv
+        s = strides or [None] * 5
+        return lib.fa_bwd(dtype, *p, B, Sq, Sk, Hq, Hkv, D, *s, o if o is not None else ob, ws, wsb, None)
+    assert bw(dtype=3) == 1
+    assert bw(Hq=3, Hkv=2) == 1
+    assert bw(D=32) == 2                      # backward: D 64 or 128
+    assert bw(D=96) == 2
+    assert bw(D=256) == 2
+    assert bw(Sq=-1) == 1
+    assert bw(wsb=100) == 3                   # 2*2*8*4 = 128 -> 256 bytes needed
+    assert bw(ws=None) == 1
+    assert bw(ws=ctypes.c_void_p((1 << 21) + 4)) == 2
+    assert bw(ptrs=[None] + [FAKE] * 8) == 1  # dout
+    assert bw(ptrs=[FAKE] * 8 + [None]) == 1  # dv
+    assert bw(ptrs=[FAKE, ctypes.c_void_p((1 << 20) + 8)] + [FAKE] * 7) == 2   # q misaligned
+    assert bw(strides=[(ctypes.c_int64 * 3)(8 * 128, 128, 60)] + [None] * 4) == 2
+    assert bw(strides=[None] * 4 + [(ctypes.c_int64 * 3)(-8, 128, 64)]) == 1  # dout stride
+    o2, keep2 = _opts(wl=-2)
+    assert bw(o=o2) == 1
+    o3, keep3 = _opts(softcap=-1.0)
+    assert bw(o=o3) == 1
+    assert bw(B=0) == 0                       # nothing to do
+    assert bw(Sq=0, Sk=0) == 0
+    assert bw(Sq=0, ws=None, wsb=0, ptrs=[None, None, FAKE, FAKE, None, None, None, FAKE, None]) == 1
+    # (Sq = 0 still writes dk = dv = 0, so dv must be given)
 
 
 def test_combine_rejects(lib):
