@@ -13,8 +13,10 @@ prefill kernel's mean duration from HIP events on the launch stream; the
 decode figure (GB/s of algorithmic K/V/q/out/block-table bytes over the
 decode + combine time) rides along in "decode".  "decode_append" times the
 same decode call with a one-token KV append per sequence (fwd_kvcache with
-k=, v=), and "prefill_fp8" the prefill on the same inputs converted to fp8
-e4m3, both after the timed steps.  "cpu_baseline" times the float64 CPU oracle
+k=, v=), "prefill_fp8" the prefill on the same inputs converted to fp8
+e4m3, and "backward" the gradients of that prefill (fa_bwd with a seeded
+dout, TFLOP/s at 10·D per allowed pair: the five products S, dP, dV, dK, dQ),
+all after the timed steps.  "cpu_baseline" times the float64 CPU oracle
 on a bounded sample of the prefill workload.
 """
 
@@ -210,6 +212,30 @@ def main():
         f8_mean = sum(f8_ms) / len(f8_ms)
         del q8, k8, v8, out8
 
+    # backward of the timed prefill (out and lse recomputed: the fp8 leg wrote lse), seeded dout
+    b_mean = None
+    if run_p:
+        fa.fwd(q, k, v, causal=True, out=out, lse=lse)
+        gout = inputs.randn(torch.Generator().manual_seed(4400), q.shape, q.dtype).to(dev)
+        gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(fa.bwd_workspace_size(B, S, H), dtype=torch.uint8, device=dev)
+
+        def bwd_step():
+            fa.bwd(gout, q, k, v, out, lse, causal=True, dq=gq, dk=gk, dv=gv, workspace=bws)
+        for _ in range(args.warmup):
+            bwd_step()
+        torch.cuda.synchronize()
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            bev[i][0].record()
+            bwd_step()
+            bev[i][1].record()
+        torch.cuda.synchronize()
+        b_ms = [e[0].elapsed_time(e[1]) for e in bev]
+        b_mean = sum(b_ms) / len(b_ms)
+        del gout, gq, gk, gv, bws
+    b_flops = 10 * D * causal_pairs(S, S) * B * H
+
     # decode with a one-token KV append (fwd_kvcache with k=, v=): every
     # sequence's last cached token is written again from k_new/v_new (its own
     # values, so the cache is unchanged) and then attended with the rest
@@ -287,6 +313,12 @@ def main():
         "prefill_fp8": None if f8_mean is None else {
             "value": round(p_flops / (f8_mean * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_mean": round(f8_mean, 5),
             "dtype": "fp8 e4m3 in (Q K^T on fp8 MFMA), bf16 P V and out"},
+        "backward": None if b_mean is None else {
+            "value": round(b_flops / (b_mean * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_mean": round(b_mean, 5),
+            "flops": b_flops, "dtype": "fp16",
+            "roofline": {"bound": "mfma", "achieved": round(b_flops / (b_mean * 1e-3) / 1e12, 2),
+                         "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(b_flops / (b_mean * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}},
         "decode_append": None if a_mean is None else {
             "value": round(a_bytes / (a_mean * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_mean": round(a_mean, 5),
             "bytes": a_bytes, "new_tokens_per_sequence": 1,
