@@ -57,7 +57,8 @@ def kernel_source_hash(which: str = "prefill") -> str:
     """Short hash of the sources a kernel is built from; stored traffic figures
     are used only while it matches."""
     files = {"prefill": ("prefill.hip", "fa_device.hpp", "fa_kernels.hpp"),
-             "decode": ("decode.hip", "combine.hip", "fa_device.hpp", "fa_kernels.hpp")}[which]
+             "decode": ("decode.hip", "combine.hip", "fa_device.hpp", "fa_kernels.hpp"),
+             "backward": ("backward.hip", "fa_device.hpp", "fa_kernels.hpp")}[which]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "exact_attention_forward_fa_amd", "csrc", f), "rb") as fh:
@@ -274,7 +275,7 @@ def main():
 
     # HBM bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE,
     # scaled by a device copy), only while the kernel sources are unchanged
-    traffic = d_traffic = None
+    traffic = d_traffic = b_traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
@@ -282,8 +283,10 @@ def main():
             traffic = tr["prefill_bytes_per_launch"]
         if tr.get("decode_source_sha") == kernel_source_hash("decode"):
             d_traffic = tr["decode_bytes_per_call"]
+        if tr.get("backward_source_sha") == kernel_source_hash("backward"):
+            b_traffic = tr.get("backward_bytes_per_call")
     except (OSError, ValueError, KeyError):
-        traffic = d_traffic = None
+        traffic = d_traffic = b_traffic = None
 
     line = {
         "metric": "attn fwd TFLOP/s (causal, B4 S4096 H32 D64 fp16) + paged decode HBM GB/s",
@@ -318,7 +321,8 @@ def main():
             "flops": b_flops, "dtype": "fp16",
             "roofline": {"bound": "mfma", "achieved": round(b_flops / (b_mean * 1e-3) / 1e12, 2),
                          "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(b_flops / (b_mean * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}},
+                         "frac": round(b_flops / (b_mean * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+                         "traffic": b_traffic}},
         "decode_append": None if a_mean is None else {
             "value": round(a_bytes / (a_mean * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_mean": round(a_mean, 5),
             "bytes": a_bytes, "new_tokens_per_sequence": 1,
