@@ -98,11 +98,37 @@ __device__ __forceinline__ float score_l2(float x, float dist, float sl2, float 
 
 constexpr int kBig = 1 << 30;
 
+// Workgroup shapes and register budgets (waves per SIMD the compiler targets).
+#ifndef FA_BWD_KV_NW64
+#define FA_BWD_KV_NW64 4
+#endif
+#ifndef FA_BWD_KV_WPE64
+#define FA_BWD_KV_WPE64 2
+#endif
+#ifndef FA_BWD_KV_NW128
+#define FA_BWD_KV_NW128 4
+#endif
+#ifndef FA_BWD_KV_WPE128
+#define FA_BWD_KV_WPE128 1
+#endif
+#ifndef FA_BWD_Q_NW64
+#define FA_BWD_Q_NW64 4
+#endif
+#ifndef FA_BWD_Q_NW128
+#define FA_BWD_Q_NW128 8
+#endif
+#ifndef FA_BWD_Q_WPE64
+#define FA_BWD_Q_WPE64 3
+#endif
+#ifndef FA_BWD_Q_WPE128
+#define FA_BWD_Q_WPE128 2
+#endif
+
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup = NW waves x 32 keys; query tiles of 64 rows through LDS
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? FA_BWD_KV_WPE128 : FA_BWD_KV_WPE64)))
 void bwd_dkdv_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -324,7 +350,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
 // dQ: workgroup = NW waves x 32 queries; key tiles of 64 rows through LDS
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? FA_BWD_Q_WPE128 : FA_BWD_Q_WPE64)))
 void bwd_dq_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -496,11 +522,11 @@ void bwd_dq_kernel(BackwardParams p) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <int D> constexpr int bwd_dkdv_waves() { return D >= 128 ? 4 : 8; }
-constexpr int kBwdDqWaves = 8;
+template <int D> constexpr int bwd_dkdv_waves() { return D >= 128 ? FA_BWD_KV_NW128 : FA_BWD_KV_NW64; }
+template <int D> constexpr int bwd_dq_waves() { return D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64; }
 
-int backward_block_n(int D) { return (D >= 128 ? 4 : 8) * 32; }
-int backward_block_m(int) { return kBwdDqWaves * 32; }
+int backward_block_n(int D) { return (D >= 128 ? FA_BWD_KV_NW128 : FA_BWD_KV_NW64) * 32; }
+int backward_block_m(int D) { return (D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64) * 32; }
 
 template <class E, int D, bool SOFTCAP, bool ALIBI>
 hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
@@ -517,8 +543,8 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
   if (gq > 0) {
     BackwardParams pq = p;
     pq.remap_xcd = gq % 8 == 0;
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, kBwdDqWaves, SOFTCAP, ALIBI>), dim3((unsigned)gq), dim3(kBwdDqWaves * 64),
-                       0, s, pq);
+    constexpr int NWQ = bwd_dq_waves<D>();
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, NWQ, SOFTCAP, ALIBI>), dim3((unsigned)gq), dim3(NWQ * 64), 0, s, pq);
     return hipGetLastError();
   }
   return hipSuccess;
