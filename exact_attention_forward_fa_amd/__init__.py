@@ -10,6 +10,7 @@ and the current stream.  The calls mirror the interface described on
 * ``fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, ...)``
 * ``combine(out_partial, lse_partial)``
 * ``bwd(dout, q, k, v, out, lse, ...)`` -> (dq, dk, dv)    gradients of ``fwd``
+* ``bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q, max_k, ...)``  of ``fwd_varlen``
 * ``attention(q, k, v, ...)``      -> out, differentiable (``fwd`` + ``bwd``)
 
 There is no fallback: if libfa.so is missing or a tensor is not on the GPU the
@@ -23,7 +24,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "bwd", "attention", "kvcache_workspace_size",
+__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "bwd", "bwd_varlen", "attention", "kvcache_workspace_size",
            "kvcache_num_splits", "bwd_workspace_size", "library_path", "load_library", "FaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,9 @@ def load_library():
     lib.fa_bwd_workspace_size.restype = Z
     lib.fa_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I64P, I64P, I64P, I64P, I64P, OP, P, Z, P]
     lib.fa_bwd.restype = I
+    lib.fa_bwd_varlen.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                  I64P, I64P, I64P, I64P, I64P, OP, P, Z, P]
+    lib.fa_bwd_varlen.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -383,6 +387,48 @@ def bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(
                       _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)), _strides(v, (0, 1, 2)),
                       _strides(out, (0, 1, 2)), _strides(dout, (0, 1, 2)), ob,
                       _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwd_varlen(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+               softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None,
+               dq=None, dk=None, dv=None, workspace=None, deterministic=True):
+    """Gradients of ``fwd_varlen``: returns (dq [total_q,Hq,D], dk, dv [total_k,Hkv,D]).
+    ``out`` and ``lse`` ([Hq, total_q]) are what ``fwd_varlen`` returned."""
+    _need_gpu(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k)
+    if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise ValueError("dout, q, k, v, out must share dtype float16 or bfloat16")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("expected q, out, dout [total_q,Hq,D] and k, v [total_k,Hkv,D]")
+    if any(t.stride(-1) != 1 for t in (dout, q, k, v, out)):
+        raise ValueError("head_dim must be contiguous")
+    total_q, Hq, D = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [Hq, total_q]")
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, k.shape)):
+        if t is not None and (t.shape != shape or t.dtype != q.dtype or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous tensor like its input")
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=q.dtype, device=q.device) if dv is None else dv
+    lib = load_library()
+    need = int(lib.fa_bwd_workspace_size(1, total_q, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    _check(lib.fa_bwd_varlen(_DTYPES[q.dtype], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q.contiguous()),
+                             _ptr(cu_seqlens_k.contiguous()), B, int(max_seqlen_q), int(max_seqlen_k),
+                             total_q, total_k, Hq, Hkv, D, _strides(q, (0, 1)), _strides(k, (0, 1)),
+                             _strides(v, (0, 1)), _strides(out, (0, 1)), _strides(dout, (0, 1)), ob,
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -59,14 +59,14 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
   constexpr int CH = D / 8, RPB = 256 / CH;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CH;   // (b, i, h), h fastest
   const int c = threadIdx.x % CH;
-  const int64_t nrows = (int64_t)p.B * p.Sq * p.Hq;
+  const int64_t nrows = (int64_t)p.delta_B * p.delta_S * p.Hq;
   float acc = 0.f;
   int64_t b = 0, i = 0, h = 0;
   if (row < nrows) {
     h = row % p.Hq;
     const int64_t bi = row / p.Hq;
-    i = bi % p.Sq;
-    b = bi / p.Sq;
+    i = bi % p.delta_S;
+    b = bi / p.delta_S;
     const V8 x = *(const V8*)((const T*)p.out + b * p.o_sb + i * p.o_ss + h * p.o_sh + c * 8);
     const V8 y = *(const V8*)((const T*)p.dout + b * p.do_sb + i * p.do_ss + h * p.do_sh + c * 8);
 #pragma unroll
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
   }
 #pragma unroll
   for (int m = CH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < nrows && c == 0) p.delta[(b * p.Hq + h) * p.Sq + i] = acc;
+  if (row < nrows && c == 0) p.delta[b * p.dl_sb + h * p.dl_sh + i] = acc;
 }
 
 // Score of one (query, key) pair in log2 units from the raw product x = q·k, and
@@ -155,8 +155,17 @@ void bwd_dkdv_kernel(BackwardParams p) {
   const int head = id / p.n_ktiles;
   const int kt = id - head * p.n_ktiles;
   const int b = head / p.Hkv, hk = head - b * p.Hkv;
-  const int sq = p.Sq, sk = p.Sk, shift = sk - sq;
+  int sq = p.Sq, sk = p.Sk, qbase = 0, kbase = 0;
+  if (p.cu_seqlens_q) {
+    qbase = p.cu_seqlens_q[b];
+    sq = p.cu_seqlens_q[b + 1] - qbase;
+    kbase = p.cu_seqlens_k[b];
+    sk = p.cu_seqlens_k[b + 1] - kbase;
+  }
+  const int shift = sk - sq;
   const int n0 = kt * BNK;
+  if (n0 >= sk) return;                    // varlen: past this sequence's keys
+  const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
 
   // the lane's key and the query rows that may attend it: i in [a_j, b_j]
   const int j = n0 + wave * 32 + l32;
@@ -179,8 +188,8 @@ void bwd_dkdv_kernel(BackwardParams p) {
   // (lane <-> key, d = 16dc + 8hi .. +7)
   V8 kr[DC], vr[DC];
   {
-    const T* kp = (const T*)p.k + (int64_t)b * p.k_sb + (int64_t)jc * p.k_ss + (int64_t)hk * p.k_sh + hi * 8;
-    const T* vp = (const T*)p.v + (int64_t)b * p.v_sb + (int64_t)jc * p.v_ss + (int64_t)hk * p.v_sh + hi * 8;
+    const T* kp = (const T*)p.k + bq * p.k_sb + (int64_t)(kbase + jc) * p.k_ss + (int64_t)hk * p.k_sh + hi * 8;
+    const T* vp = (const T*)p.v + bq * p.v_sb + (int64_t)(kbase + jc) * p.v_ss + (int64_t)hk * p.v_sh + hi * 8;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       kr[dc] = *(const V8*)(kp + dc * 16);
@@ -199,8 +208,8 @@ void bwd_dkdv_kernel(BackwardParams p) {
     const int g = it / nt, t = t_lo + (it - g * nt);
     const int hq = hk * p.group + g;
     const int r0 = t * BMQ;
-    const T* qp = (const T*)p.q + (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh;
-    const T* gp = (const T*)p.dout + (int64_t)b * p.do_sb + (int64_t)hq * p.do_sh;
+    const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
+    const T* gp = (const T*)p.dout + bq * p.do_sb + (int64_t)qbase * p.do_ss + (int64_t)hq * p.do_sh;
 #pragma unroll
     for (int i = 0; i < LQ; ++i) {
       const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
@@ -211,8 +220,8 @@ void bwd_dkdv_kernel(BackwardParams p) {
     if (tid < BMQ) {
       const int row = r0 + tid;
       const int rc = min(row, sq - 1);
-      const float l = p.lse[(int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + rc];
-      const float d = p.delta[((int64_t)b * p.Hq + hq) * sq + rc];
+      const float l = p.lse[bq * p.lse_sb + (int64_t)hq * p.lse_sh + qbase + rc];
+      const float d = p.delta[bq * p.dl_sb + (int64_t)hq * p.dl_sh + qbase + rc];
       lst = (row < sq && l != kNegInf) ? l * kLog2e : __builtin_inff();
       est = row < sq ? d : 0.f;
     }
@@ -331,8 +340,8 @@ void bwd_dkdv_kernel(BackwardParams p) {
 
   // ---- epilogue: register r of dk[db] / dv[db] is key n0 + 32w + 8(r/4) + 4hi + r%4,
   // column d = 32db + l32
-  T* dkp = (T*)p.dk + (int64_t)b * p.dk_sb + (int64_t)hk * p.dk_sh;
-  T* dvp = (T*)p.dv + (int64_t)b * p.dv_sb + (int64_t)hk * p.dv_sh;
+  T* dkp = (T*)p.dk + bq * p.dk_sb + (int64_t)kbase * p.dk_ss + (int64_t)hk * p.dk_sh;
+  T* dvp = (T*)p.dv + bq * p.dv_sb + (int64_t)kbase * p.dv_ss + (int64_t)hk * p.dv_sh;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = n0 + wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -373,8 +382,17 @@ void bwd_dq_kernel(BackwardParams p) {
   const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);   // last (longest) query tiles first
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
-  const int sq = p.Sq, sk = p.Sk, shift = sk - sq;
+  int sq = p.Sq, sk = p.Sk, qbase = 0, kbase = 0;
+  if (p.cu_seqlens_q) {
+    qbase = p.cu_seqlens_q[b];
+    sq = p.cu_seqlens_q[b + 1] - qbase;
+    kbase = p.cu_seqlens_k[b];
+    sk = p.cu_seqlens_k[b + 1] - kbase;
+  }
+  const int shift = sk - sq;
   const int m0 = qt * BM;
+  if (m0 >= sq) return;                    // varlen: past this sequence's queries
+  const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
 
   // the lane's query row and its allowed keys [j_lo, j_hi]
   const int i = m0 + wave * 32 + l32;
@@ -397,24 +415,24 @@ void bwd_dq_kernel(BackwardParams p) {
   // Q and dO rows of the lane's query: B operands of Sᵀ = K Qᵀ and dPᵀ = V dOᵀ
   V8 qr[DC], gr[DC];
   {
-    const T* qp = (const T*)p.q + (int64_t)b * p.q_sb + (int64_t)ic * p.q_ss + (int64_t)hq * p.q_sh + hi * 8;
-    const T* gp = (const T*)p.dout + (int64_t)b * p.do_sb + (int64_t)ic * p.do_ss + (int64_t)hq * p.do_sh + hi * 8;
+    const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)(qbase + ic) * p.q_ss + (int64_t)hq * p.q_sh + hi * 8;
+    const T* gp = (const T*)p.dout + bq * p.do_sb + (int64_t)(qbase + ic) * p.do_ss + (int64_t)hq * p.do_sh + hi * 8;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       qr[dc] = *(const V8*)(qp + dc * 16);
       gr[dc] = *(const V8*)(gp + dc * 16);
     }
   }
-  const float lse = p.lse[(int64_t)b * p.lse_sb + (int64_t)hq * p.lse_sh + ic];
+  const float lse = p.lse[bq * p.lse_sb + (int64_t)hq * p.lse_sh + qbase + ic];
   const float L = (row_ok && lse != kNegInf) ? lse * kLog2e : __builtin_inff();
-  const float Dl = row_ok ? p.delta[((int64_t)b * p.Hq + hq) * sq + ic] : 0.f;
+  const float Dl = row_ok ? p.delta[bq * p.dl_sb + (int64_t)hq * p.dl_sh + qbase + ic] : 0.f;
   const float sl2 = p.scale * kLog2e;
   const float cap_l2 = p.softcap * kLog2e;
   const float cap_in = 2.f * p.scale * kLog2e / (SOFTCAP ? p.softcap : 1.f);
   const float slope_l2 = ALIBI ? p.alibi[hq] * kLog2e : 0.f;
 
-  const T* kp = (const T*)p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
-  const T* vp = (const T*)p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+  const T* kp = (const T*)p.k + bq * p.k_sb + (int64_t)kbase * p.k_ss + (int64_t)hk * p.k_sh;
+  const T* vp = (const T*)p.v + bq * p.v_sb + (int64_t)kbase * p.v_ss + (int64_t)hk * p.v_sh;
   u32x4 kst[LK], vst[LK];
   auto gload = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
@@ -508,7 +526,7 @@ void bwd_dq_kernel(BackwardParams p) {
   }
 
   // ---- epilogue: register r of dq[db] is query m0 + 32w + 8(r/4) + 4hi + r%4, d = 32db + l32
-  T* dqp = (T*)p.dq + (int64_t)b * p.dq_sb + (int64_t)hq * p.dq_sh;
+  T* dqp = (T*)p.dq + bq * p.dq_sb + (int64_t)qbase * p.dq_ss + (int64_t)hq * p.dq_sh;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = m0 + wave * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -553,7 +571,7 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
 template <class E, int D>
 hipError_t launch_bwd_d(const BackwardParams& p, hipStream_t s) {
   constexpr int RPB = 256 / (D / 8);
-  const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
+  const int64_t rows = (int64_t)p.delta_B * p.delta_S * p.Hq;
   if (rows > 0) {
     hipLaunchKernelGGL((bwd_delta_kernel<E, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();

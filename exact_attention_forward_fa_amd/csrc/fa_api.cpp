@@ -476,7 +476,10 @@ fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k,
   p.dk_sb = kd[0]; p.dk_ss = kd[1]; p.dk_sh = kd[2];
   p.dv_sb = kd[0]; p.dv_ss = kd[1]; p.dv_sh = kd[2];
   p.lse_sb = (int64_t)Hq * Sq; p.lse_sh = Sq;
+  p.dl_sb = (int64_t)Hq * Sq; p.dl_sh = Sq;
+  p.cu_seqlens_q = nullptr; p.cu_seqlens_k = nullptr;
   p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.delta_B = B; p.delta_S = Sq;
   p.scale = scale;
   p.softcap = opts ? opts->softcap : 0.f;
   p.alibi = opts ? opts->alibi_slopes : nullptr;
@@ -486,6 +489,78 @@ fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k,
   p.n_ktiles = (int)nkt;
   p.n_qtiles = (int)nqt;
   return launch_status(fa::launch_backward((fa::Dtype)dtype, D, p, (hipStream_t)stream), "backward launch");
+}
+
+fa_status fa_bwd_varlen(fa_dtype dtype, const void* dout, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                        int max_seqlen_k, int total_q, int total_k, int Hq, int Hkv, int D,
+                        const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                        const int64_t* o_stride, const int64_t* do_stride, const fa_attn_opts* opts,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(dtype, Hq, Hkv, D);
+  if (st) return st;
+  if (D != 64 && D != 128) return fail(FA_ERR_UNSUPPORTED, "backward head_dim %d not built (64 or 128)", D);
+  if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  float scale;
+  if ((st = check_opts(opts, D, &scale))) return st;
+  if (B == 0 || (total_q == 0 && total_k == 0)) return ok();
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(FA_ERR_INVALID_ARGUMENT, "null cu_seqlens pointer");
+  if (total_q > 0 && (!q || !dout || !out || !lse || !dq))
+    return fail(FA_ERR_INVALID_ARGUMENT, "null q/dout/out/lse/dq pointer");
+  if (total_k > 0 && (!k || !v || !dk || !dv)) return fail(FA_ERR_INVALID_ARGUMENT, "null k/v/dk/dv pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(FA_ERR_UNSUPPORTED, "q/k/v/out/dout/dq/dk/dv must be 16-byte aligned");
+  const int64_t qd[2] = {(int64_t)Hq * D, D};
+  const int64_t kd[2] = {(int64_t)Hkv * D, D};
+  const int64_t* qs = q_stride ? q_stride : qd;
+  const int64_t* ks = k_stride ? k_stride : kd;
+  const int64_t* vs = v_stride ? v_stride : kd;
+  const int64_t* os = o_stride ? o_stride : qd;
+  const int64_t* gs = do_stride ? do_stride : qd;
+  if ((st = check_strides("q", qs, 2)) || (st = check_strides("k", ks, 2)) || (st = check_strides("v", vs, 2)) ||
+      (st = check_strides("out", os, 2)) || (st = check_strides("dout", gs, 2)))
+    return st;
+  const size_t need = fa_bwd_workspace_size(1, total_q, Hq);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_INVALID_ARGUMENT, "null workspace");
+    if (!aligned16(workspace)) return fail(FA_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  const int bn = fa::backward_block_n(D), bm = fa::backward_block_m(D);
+  const int64_t nkt = (max_seqlen_k + bn - 1) / bn, nqt = (max_seqlen_q + bm - 1) / bm;
+  if (nkt * B * (int64_t)Hkv > kMaxGrid || nqt * B * (int64_t)Hq > kMaxGrid ||
+      ((int64_t)total_q * Hq * (D / 8) + 255) / 256 > kMaxGrid)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+
+  fa::BackwardParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.delta = (float*)workspace;
+  p.q_sb = 0; p.q_ss = qs[0]; p.q_sh = qs[1];
+  p.k_sb = 0; p.k_ss = ks[0]; p.k_sh = ks[1];
+  p.v_sb = 0; p.v_ss = vs[0]; p.v_sh = vs[1];
+  p.o_sb = 0; p.o_ss = os[0]; p.o_sh = os[1];
+  p.do_sb = 0; p.do_ss = gs[0]; p.do_sh = gs[1];
+  p.dq_sb = 0; p.dq_ss = qd[0]; p.dq_sh = qd[1];
+  p.dk_sb = 0; p.dk_ss = kd[0]; p.dk_sh = kd[1];
+  p.dv_sb = 0; p.dv_ss = kd[0]; p.dv_sh = kd[1];
+  p.lse_sb = 0; p.lse_sh = total_q;
+  p.dl_sb = 0; p.dl_sh = total_q;
+  p.cu_seqlens_q = cu_seqlens_q; p.cu_seqlens_k = cu_seqlens_k;
+  p.B = B; p.Sq = max_seqlen_q; p.Sk = max_seqlen_k; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
+  p.delta_B = 1; p.delta_S = total_q;
+  p.scale = scale;
+  p.softcap = opts ? opts->softcap : 0.f;
+  p.alibi = opts ? opts->alibi_slopes : nullptr;
+  p.causal = opts ? (opts->causal != 0) : 0;
+  p.wl = opts ? opts->window_left : -1;
+  p.wr = opts ? opts->window_right : -1;
+  p.n_ktiles = (int)nkt;
+  p.n_qtiles = (int)nqt;
+  return launch_status(fa::launch_backward((fa::Dtype)dtype, D, p, (hipStream_t)stream), "varlen backward launch");
 }
 
 fa_status fa_combine(const float* out_partial, const float* lse_partial, int B, int S, int H, int D,

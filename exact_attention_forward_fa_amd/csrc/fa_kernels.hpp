@@ -102,7 +102,9 @@ struct BackwardParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;                // workspace [B, Hq, Sq]: rowsum(dout * out)
+  float* delta;                // workspace: rowsum(dout * out), element (b, h, i) at b*dl_sb + h*dl_sh + row_base + i
+  const int* cu_seqlens_q;     // varlen: [B+1] prefix sums (nullptr for dense)
+  const int* cu_seqlens_k;
   // element strides: batch, sequence, head (head_dim stride is 1)
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
@@ -112,8 +114,10 @@ struct BackwardParams {
   int64_t dq_sb, dq_ss, dq_sh;
   int64_t dk_sb, dk_ss, dk_sh;
   int64_t dv_sb, dv_ss, dv_sh;
-  int64_t lse_sb, lse_sh;
-  int B, Sq, Sk, Hq, Hkv, group;
+  int64_t lse_sb, lse_sh;      // as for the forward: element (b, h, i) at b*lse_sb + h*lse_sh + row_base + i
+  int64_t dl_sb, dl_sh;
+  int B, Sq, Sk, Hq, Hkv, group;   // varlen: Sq/Sk hold max_seqlen_q/k
+  int delta_B, delta_S;        // rows of the delta kernel: (delta_B, delta_S, Hq); varlen (1, total_q)
   float scale;
   float softcap;
   const float* alibi;

@@ -223,6 +223,25 @@ fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k,
                  const int64_t* o_stride, const int64_t* do_stride, const fa_attn_opts* opts,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of fa_fwd_varlen (packed sequences, "FlashAttention 常用接口简单介绍",
+ * §3.2), with the conventions of fa_bwd.
+ *   dout, q, out [total_q, Hq, D]; k, v [total_k, Hkv, D]; lse [Hq, total_q]
+ *   float32 as written by fa_fwd_varlen; dq [total_q, Hq, D], dk and dv
+ *   [total_k, Hkv, D] contiguous.  cu_seqlens_q/k, B and max_seqlen_q/k as for
+ *   fa_fwd_varlen; *_stride: (token, head) element strides, NULL = contiguous.
+ *   workspace: at least fa_bwd_workspace_size(1, total_q, Hq) bytes.
+ *   Each sequence's gradients equal those of fa_bwd on that sequence alone,
+ *   bit for bit.
+ */
+fa_status fa_bwd_varlen(fa_dtype dtype, const void* dout, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                        int max_seqlen_k, int total_q, int total_k, int Hq, int Hkv, int D,
+                        const int64_t* q_stride, const int64_t* k_stride, const int64_t* v_stride,
+                        const int64_t* o_stride, const int64_t* do_stride, const fa_attn_opts* opts,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(fa_status status);
 /* Detail of the last error returned on the calling thread ("" if none). */

@@ -202,6 +202,23 @@ def test_bwd_rejects(lib):
     # (Sq = 0 still writes dk = dv = 0, so dv must be given)
 
 
+def test_bwd_varlen_rejects(lib):
+    ob, keep = _opts()
+    WS = ctypes.c_void_p(1 << 21)
+
+    def bv(B=2, mq=8, mk=8, tq=12, tk=12, D=64, ws=WS, wsb=1 << 20, cu=FAKE, ptrs=None):
+        p = ptrs or [FAKE] * 9
+        return lib.fa_bwd_varlen(0, *p, cu, cu, B, mq, mk, tq, tk, 2, 2, D, None, None, None, None, None, ob,
+                                 ws, wsb, None)
+    assert bv(D=96) == 2
+    assert bv(tq=-1) == 1
+    assert bv(cu=None) == 1
+    assert bv(wsb=16) == 3                    # 2 heads * 12 rows * 4 bytes -> 256 needed
+    assert bv(ptrs=[FAKE] * 8 + [None]) == 1  # dv
+    assert bv(B=0) == 0
+    assert bv(tq=0, tk=0) == 0
+
+
 def test_combine_rejects(lib):
     f = lambda **k: lib.fa_combine(FAKE, FAKE, 1, 1, 1, k.get("D", 64), k.get("ns", 4), None, None,
                                    k.get("dt", 0), k.get("out", FAKE), None, None, None)

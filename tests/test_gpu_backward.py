@@ -162,6 +162,56 @@ def test_backward_keys_no_query_sees_get_zero():
     check_grads(got, want, torch.float16, "unseen keys")
 
 
+# ---------------------------------------------------------------- packed sequences
+
+VARLEN = [
+    # (lengths_q, lengths_k, Hq, Hkv, D, dtype, options)
+    ([130, 0, 257, 64], [130, 0, 257, 64], 4, 2, 64, torch.float16, dict(causal=True)),
+    ([40, 300, 1], [200, 100, 77], 2, 2, 128, torch.bfloat16, dict(causal=True, softcap=3.0)),
+    ([96, 33], [96, 0], 4, 1, 64, torch.bfloat16, dict(window=(16, 8), alibi_slopes=SLOPES)),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: f"q{c[0]}-k{c[1]}-d{c[4]}")
+def test_backward_varlen_equals_per_sequence_dense(case):
+    """Each packed sequence gets the float64 oracle's gradients within the bar,
+    and exactly the bits fa_bwd gives that sequence on its own."""
+    lq, lk, Hq, Hkv, D, dt, o = case
+    print("case varlen", case[:6], flush=True)
+    q, k, v, cq, ck = inputs.varlen_pack(lq, lk, Hq, Hkv, D, dt, seed=4500 + sum(lq))
+    g = inputs.randn(torch.Generator().manual_seed(4501), q.shape, dt)
+    opts = dict(o)
+    if opts.get("alibi_slopes") == SLOPES:
+        opts["alibi_slopes"] = inputs.alibi_slopes(Hq)
+    sl = opts.get("alibi_slopes")
+    kw = dict(softmax_scale=opts.get("softmax_scale"), causal=opts.get("causal", False),
+              window_size=opts.get("window", (-1, -1)), softcap=opts.get("softcap", 0.0),
+              alibi_slopes=None if sl is None else sl.to(DEV))
+    qd, kd, vd, gd, cqd, ckd = (t.to(DEV) for t in (q, k, v, g, cq, ck))
+    out, lse = fa.fwd_varlen(qd, kd, vd, cqd, ckd, max(lq), max(lk), **kw)
+    dq, dk, dv = fa.bwd_varlen(gd, qd, kd, vd, out, lse, cqd, ckd, max(lq), max(lk), **kw)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for b in range(len(lq)):
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        if q1 == q0 and k1 == k0:
+            continue
+        if k1 > k0 and q1 > q0:
+            want = oracle(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], g[None, q0:q1], opts)
+            check_grads((dq[None, q0:q1], dk[None, k0:k1], dv[None, k0:k1]), want, dt, f"varlen seq {b}")
+            # the same sequence alone through the dense call
+            sd = [t.to(DEV).contiguous() for t in (q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], g[None, q0:q1])]
+            o1, l1 = fa.fwd(sd[0], sd[1], sd[2], **kw)
+            a = fa.bwd(sd[3], sd[0], sd[1], sd[2], o1, l1, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(a[0].cpu()[0], dq[q0:q1]) and torch.equal(a[1].cpu()[0], dk[k0:k1]) \
+                and torch.equal(a[2].cpu()[0], dv[k0:k1]), f"sequence {b} differs from its dense backward"
+        else:
+            # one side empty: the other side's gradients are zero
+            assert torch.count_nonzero(dq[q0:q1]) == 0 and torch.count_nonzero(dk[k0:k1]) == 0 \
+                and torch.count_nonzero(dv[k0:k1]) == 0
+
+
 # ---------------------------------------------------------------- full sizes, sampled heads
 
 @pytest.mark.parametrize("name,heads", [("c3_causal", [(1, 7), (3, 30)]), ("c4_gqa", [(1, 5)])])
