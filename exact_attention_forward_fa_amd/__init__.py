@@ -12,6 +12,7 @@ and the current stream.  The calls mirror the interface described on
 * ``bwd(dout, q, k, v, out, lse, ...)`` -> (dq, dk, dv)    gradients of ``fwd``
 * ``bwd_varlen(dout, q, k, v, out, lse, cu_q, cu_k, max_q, max_k, ...)``  of ``fwd_varlen``
 * ``attention(q, k, v, ...)``      -> out, differentiable (``fwd`` + ``bwd``)
+* ``attention_varlen(q, k, v, cu_q, cu_k, max_q, max_k, ...)`` -> out, differentiable
 
 There is no fallback: if libfa.so is missing or a tensor is not on the GPU the
 call raises.
@@ -24,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "bwd", "bwd_varlen", "attention", "kvcache_workspace_size",
+__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "bwd", "bwd_varlen", "attention", "attention_varlen", "kvcache_workspace_size",
            "kvcache_num_splits", "bwd_workspace_size", "library_path", "load_library", "FaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -454,3 +455,32 @@ def attention(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), s
     """Differentiable dense attention: ``fwd`` forward, ``bwd`` backward (weights
     recomputed from the saved lse).  Returns out [B, Sq, Hq, D]."""
     return _Attention.apply(q, k, v, softmax_scale, causal, tuple(window_size), softcap, alibi_slopes)
+
+
+class _AttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                window_size, softcap, alibi_slopes):
+        out, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                              softmax_scale=softmax_scale, causal=causal, window_size=window_size,
+                              softcap=softcap, alibi_slopes=alibi_slopes)
+        ctx.save_for_backward(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k)
+        ctx.opts = (max_seqlen_q, max_seqlen_k, softmax_scale, causal, window_size, softcap, alibi_slopes)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
+        max_q, max_k, softmax_scale, causal, window_size, softcap, alibi_slopes = ctx.opts
+        dq, dk, dv = bwd_varlen(dout.contiguous(), q, k, v, out, lse, cu_q, cu_k, max_q, max_k,
+                                softmax_scale=softmax_scale, causal=causal, window_size=window_size,
+                                softcap=softcap, alibi_slopes=alibi_slopes)
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale=None,
+                     causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None):
+    """Differentiable packed attention: ``fwd_varlen`` forward, ``bwd_varlen``
+    backward.  Returns out [total_q, Hq, D]."""
+    return _AttentionVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q), int(max_seqlen_k),
+                                  softmax_scale, causal, tuple(window_size), softcap, alibi_slopes)

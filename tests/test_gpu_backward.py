@@ -212,6 +212,45 @@ def test_backward_varlen_equals_per_sequence_dense(case):
                 and torch.count_nonzero(dv[k0:k1]) == 0
 
 
+def test_backward_varlen_autograd_wrapper_matches_bwd_varlen():
+    print("case varlen autograd", flush=True)
+    lq = [70, 129, 1]
+    q, k, v, cq, ck = inputs.varlen_pack(lq, lq, 4, 2, 128, torch.float16, seed=4600)
+    g = inputs.randn(torch.Generator().manual_seed(4601), q.shape, q.dtype)
+    qd, kd, vd, gd, cqd, ckd = (t.to(DEV) for t in (q, k, v, g, cq, ck))
+    out, lse = fa.fwd_varlen(qd, kd, vd, cqd, ckd, max(lq), max(lq), causal=True)
+    want = fa.bwd_varlen(gd, qd, kd, vd, out, lse, cqd, ckd, max(lq), max(lq), causal=True)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (qd, kd, vd))
+    o2 = fa.attention_varlen(qa, ka, va, cqd, ckd, max(lq), max(lq), causal=True)
+    o2.backward(gd)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.detach(), out)
+    for a, t in zip(want, (qa, ka, va)):
+        assert torch.equal(a, t.grad)
+
+
+def test_backward_strided_views_equal_contiguous():
+    """q, k, v as views into one packed [B, S, 3, H, D] tensor and dout as a
+    transposed view: the strided call gives the bits of the contiguous call."""
+    print("case strided views", flush=True)
+    B, S, H, D = 2, 150, 4, 64
+    gen = torch.Generator().manual_seed(4700)
+    qkv = inputs.randn(gen, (B, S, 3, H, D), torch.bfloat16).to(DEV)
+    gT = inputs.randn(gen, (B, H, S, D), torch.bfloat16).to(DEV)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    dout = gT.transpose(1, 2)                                  # [B, S, H, D], strides (H*S*D, D, S*D, 1)
+    assert not q.is_contiguous() and not dout.is_contiguous()
+    out, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(dout, q, k, v, out, lse, causal=True)
+    qc, kc, vc, dc = (t.contiguous() for t in (q, k, v, dout))
+    out2, lse2 = fa.fwd(qc, kc, vc, causal=True)
+    b = fa.bwd(dc, qc, kc, vc, out2, lse2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 # ---------------------------------------------------------------- full sizes, sampled heads
 
 @pytest.mark.parametrize("name,heads", [("c3_causal", [(1, 7), (3, 30)]), ("c4_gqa", [(1, 5)])])
