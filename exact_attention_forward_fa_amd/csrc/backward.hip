@@ -108,6 +108,12 @@ constexpr int kBig = 1 << 30;
 #ifndef FA_BWD_KV_NW128
 #define FA_BWD_KV_NW128 4
 #endif
+#ifndef FA_BWD_KV_BMQ64
+#define FA_BWD_KV_BMQ64 64
+#endif
+#ifndef FA_BWD_KV_BMQ128
+#define FA_BWD_KV_BMQ128 64
+#endif
 #ifndef FA_BWD_KV_WPE128
 #define FA_BWD_KV_WPE128 1
 #endif
@@ -125,7 +131,7 @@ constexpr int kBig = 1 << 30;
 #endif
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = NW waves x 32 keys; query tiles of 64 rows through LDS
+// dK, dV: workgroup = NW waves x 32 keys; query tiles of BMQ rows through LDS
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? FA_BWD_KV_WPE128 : FA_BWD_KV_WPE64)))
@@ -133,7 +139,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
   using V2 = typename E::V2;
-  constexpr int BMQ = 64;                 // query rows per LDS tile
+  constexpr int BMQ = D >= 128 ? FA_BWD_KV_BMQ128 : FA_BWD_KV_BMQ64;   // query rows per LDS tile
   constexpr int BNK = NW * 32;            // keys per workgroup
   constexpr int CH = D / 8, DC = D / 16, DB = D / 32;
   constexpr int NT = NW * 64;
