@@ -1,7 +1,10 @@
 // Host side of the C ABI declared in include/fa.h: argument validation,
 // defaults, workspace layout and kernel launches on the caller's stream.
 // Validation never touches the HIP runtime, so every error path can be
-// exercised on a machine without a GPU.
+// exercised on a machine without a GPU.  The one exception is opt-in: with
+// the environment variable FA_DEBUG=1, the device-side index data the caller
+// promises to keep consistent (cu_seqlens, cache_seqlens, block_table) is
+// copied back and checked before anything is launched.
 #include "../../include/fa.h"
 
 #include <hip/hip_runtime.h>
@@ -9,7 +12,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
+#include <vector>
 
 #include "fa_kernels.hpp"
 
@@ -91,6 +96,71 @@ int device_cus() {
                                                hipSuccess || cus < 1)
     return 256;
   return cus;
+}
+
+// ---- FA_DEBUG=1: checks of device-side index data (synchronous, debugging only)
+bool debug_checks() {
+  const char* e = std::getenv("FA_DEBUG");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+fa_status read_ints(const int* d, size_t n, std::vector<int>& h, hipStream_t s) {
+  h.assign(n, 0);
+  if (n == 0) return FA_OK;
+  hipError_t e = hipMemcpyAsync(h.data(), d, n * sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "FA_DEBUG read of index data: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+// cu_seqlens_q/k: non-negative, non-decreasing, every length within max_seqlen,
+// the last entry within total
+fa_status debug_check_cu(const int* cu_q, const int* cu_k, int B, int max_q, int max_k, int total_q, int total_k,
+                         hipStream_t s) {
+  std::vector<int> q, k;
+  fa_status st;
+  if ((st = read_ints(cu_q, (size_t)B + 1, q, s)) || (st = read_ints(cu_k, (size_t)B + 1, k, s))) return st;
+  for (int b = 0; b <= B; ++b) {
+    if (q[b] < 0 || k[b] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "FA_DEBUG: cu_seqlens[%d] is negative", b);
+    if (b == 0) continue;
+    const int lq = q[b] - q[b - 1], lk = k[b] - k[b - 1];
+    if (lq < 0 || lk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "FA_DEBUG: cu_seqlens decrease at entry %d", b);
+    if (lq > max_q || lk > max_k)
+      return fail(FA_ERR_INVALID_ARGUMENT, "FA_DEBUG: sequence %d has %d queries / %d keys, above max_seqlen %d / %d",
+                  b - 1, lq, lk, max_q, max_k);
+  }
+  if (q[B] > total_q || k[B] > total_k)
+    return fail(FA_ERR_INVALID_ARGUMENT, "FA_DEBUG: cu_seqlens end at %d / %d, beyond total %d / %d", q[B], k[B],
+                total_q, total_k);
+  return FA_OK;
+}
+
+// cache_seqlens non-negative; when the decode runs (reads = true) every
+// sequence's cached plus new tokens fit the cache and the block-table entries
+// of the pages it reads name pages of the pool
+fa_status debug_check_cache(const int* lens, const int* bt, int bt_stride, int page_size, int num_blocks_or_smax,
+                            int B, int S_new, bool reads, hipStream_t s) {
+  std::vector<int> l, t;
+  fa_status st;
+  if ((st = read_ints(lens, (size_t)B, l, s))) return st;
+  if (bt && reads && (st = read_ints(bt, (size_t)B * bt_stride, t, s))) return st;
+  for (int b = 0; b < B; ++b) {
+    if (l[b] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "FA_DEBUG: cache_seqlens[%d] = %d is negative", b, l[b]);
+    if (!reads) continue;
+    const int64_t n = (int64_t)l[b] + S_new;
+    const int64_t cap = bt ? (int64_t)bt_stride * page_size : num_blocks_or_smax;
+    if (n > cap)
+      return fail(FA_ERR_INVALID_ARGUMENT, "FA_DEBUG: sequence %d attends %lld tokens, the cache holds %lld", b,
+                  (long long)n, (long long)cap);
+    if (!bt) continue;
+    for (int64_t pg = 0; pg * page_size < n; ++pg) {
+      const int e = t[(size_t)b * bt_stride + pg];
+      if (e < 0 || e >= num_blocks_or_smax)
+        return fail(FA_ERR_INVALID_ARGUMENT, "FA_DEBUG: block_table[%d, %lld] = %d is outside the pool of %d pages", b,
+                    (long long)pg, e, num_blocks_or_smax);
+    }
+  }
+  return FA_OK;
 }
 
 }  // namespace
@@ -229,6 +299,9 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, max_seqlen_q, device_cus());
   const int64_t nqt = (max_seqlen_q + bm - 1) / bm;
   if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (debug_checks() && (st = debug_check_cu(cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, max_seqlen_k, total_q,
+                                             total_k, (hipStream_t)stream)))
+    return st;
 
   fa::PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
@@ -330,6 +403,9 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
   }
 
   hipStream_t s = (hipStream_t)stream;
+  if (debug_checks() && (st = debug_check_cache(cache_seqlens, block_table, block_table_stride, page_size,
+                                                num_blocks_or_smax, B, S_new, Sq > 0, s)))
+    return st;
   if (S_new > 0) {
     fa::AppendParams a{};
     a.k_new = k_new; a.v_new = v_new;
@@ -535,6 +611,9 @@ fa_status fa_bwd_varlen(fa_dtype dtype, const void* dout, const void* q, const v
   if (nkt * B * (int64_t)Hkv > kMaxGrid || nqt * B * (int64_t)Hq > kMaxGrid ||
       ((int64_t)total_q * Hq * (D / 8) + 255) / 256 > kMaxGrid)
     return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (debug_checks() && (st = debug_check_cu(cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, max_seqlen_k, total_q,
+                                             total_k, (hipStream_t)stream)))
+    return st;
 
   fa::BackwardParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;

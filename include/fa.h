@@ -33,7 +33,10 @@
  *    thread-local message available from fa_last_error().  B == 0 or an empty
  *    query side is a valid no-op.  Device-side contents (monotonic cu_seqlens,
  *    in-range block_table entries, cache_seqlens within the cache) are the
- *    caller's contract and are not checked.
+ *    caller's contract and are not checked, except with the environment
+ *    variable FA_DEBUG=1: then the varlen and KV-cache calls copy them back
+ *    (synchronising the stream) and return FA_ERR_INVALID_ARGUMENT, with
+ *    nothing launched, if they are inconsistent.
  */
 #ifndef FA_H_
 #define FA_H_
