@@ -95,8 +95,26 @@ def cpu_baseline(case, n_heads: int, workers: int):
     return dict(value=flops / wall / 1e12, unit="TFLOP/s", cores=workers, kind="oracle",
                 sample=f"float64 oracle, causal, {len(pairs)} of {B * H} (batch, head) pairs of the "
                        f"B{B} S{S} H{H} D{D} prefill, all {S} rows each, {workers} single-threaded "
-                       f"worker processes, {wall:.1f} s wall; FLOPs counted as 4·D per allowed pair",
+                       f"worker processes, {wall:.1f} s wall; FLOPs counted as 4·D per allowed pair; "
+                       f"CPU {cpu_model()}, numpy {np.__version__}",
                 seconds=wall)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
 # ---------------------------------------------------------------- GPU legs
@@ -307,10 +325,13 @@ def main():
                         "pages, permuted block table, 16 splits + LSE combine (seed 1005)",
             "global_batch": B, "seq_len": S, "parallelism": "single GPU",
         },
-        "prefill": {"ms_mean": round(p_mean, 5), "ms_min": round(min(p_ms), 5), "flops": p_flops,
-                    "tflops": round(tflops, 2)},
+        "prefill": {"ms_mean": round(p_mean, 5), "ms_median": round(median(p_ms), 5), "ms_min": round(min(p_ms), 5),
+                    "flops": p_flops, "tflops": round(tflops, 2),
+                    "exps": B * H * causal_pairs(S, S),
+                    "exps_per_s": round(B * H * causal_pairs(S, S) / (p_mean * 1e-3), 1)},
         "decode": {"value": round(gbs, 1), "unit": "GB/s", "ms_mean": round(d_mean, 5),
-                   "ms_min": round(min(d_ms), 5), "bytes": d_bytes, "dtype": "bf16",
+                   "ms_median": round(median(d_ms), 5), "ms_min": round(min(d_ms), 5), "bytes": d_bytes,
+                   "dtype": "bf16",
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": d_traffic}},
         "prefill_fp8": None if f8_mean is None else {

@@ -24,3 +24,10 @@ def test_decode_bytes_counts_each_cached_token_once():
     c = dict(q=pc.q, k_pool=pc.k_pool, cache_seqlens=pc.cache_seqlens, page_size=16)
     kv = (5 + 16 + 40) * 2 * 64 * 2 * 2
     assert bench.decode_bytes(c) == kv + 2 * pc.q.numel() * 2 + (1 + 1 + 3) * 4 + 3 * 4
+
+
+def test_median_and_cpu_model():
+    import bench
+    assert bench.median([3.0, 1.0, 2.0]) == 2.0
+    assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
