@@ -72,14 +72,22 @@ fa_status check_strides(const char* name, const int64_t* s, int n) {
   return FA_OK;
 }
 
+// Window sides as the kernels take them: -1 (unbounded) or a distance.  Any
+// side of 2^30 or more reaches every key of a sequence shorter than 2^30, so
+// it is capped there, which keeps position + side inside int32 in the kernels.
+int window_side(const fa_attn_opts* o, bool left) {
+  const int w = o ? (left ? o->window_left : o->window_right) : -1;
+  return w > (1 << 30) ? (1 << 30) : w;
+}
+
 void fill_opts(fa::PrefillParams& p, const fa_attn_opts* o, float scale) {
   p.scale = scale;
   p.out_scale = 1.f;
   p.softcap = o ? o->softcap : 0.f;
   p.alibi = o ? o->alibi_slopes : nullptr;
   p.causal = o ? (o->causal != 0) : 0;
-  p.wl = o ? o->window_left : -1;
-  p.wr = o ? o->window_right : -1;
+  p.wl = window_side(o, true);
+  p.wr = window_side(o, false);
 }
 
 fa_status launch_status(hipError_t e, const char* what) {
@@ -453,8 +461,8 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
   d.softcap = opts ? opts->softcap : 0.f;
   d.alibi = opts ? opts->alibi_slopes : nullptr;
   d.causal = opts ? (opts->causal != 0) : 0;
-  d.wl = opts ? opts->window_left : -1;
-  d.wr = opts ? opts->window_right : -1;
+  d.wl = window_side(opts, true);
+  d.wr = window_side(opts, false);
   hipError_t e = fa::launch_decode((fa::Dtype)dtype, D, d, s);
   if (e != hipSuccess) return launch_status(e, "decode launch");
 
@@ -560,8 +568,8 @@ fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k,
   p.softcap = opts ? opts->softcap : 0.f;
   p.alibi = opts ? opts->alibi_slopes : nullptr;
   p.causal = opts ? (opts->causal != 0) : 0;
-  p.wl = opts ? opts->window_left : -1;
-  p.wr = opts ? opts->window_right : -1;
+  p.wl = window_side(opts, true);
+  p.wr = window_side(opts, false);
   p.n_ktiles = (int)nkt;
   p.n_qtiles = (int)nqt;
   return launch_status(fa::launch_backward((fa::Dtype)dtype, D, p, (hipStream_t)stream), "backward launch");
@@ -635,8 +643,8 @@ fa_status fa_bwd_varlen(fa_dtype dtype, const void* dout, const void* q, const v
   p.softcap = opts ? opts->softcap : 0.f;
   p.alibi = opts ? opts->alibi_slopes : nullptr;
   p.causal = opts ? (opts->causal != 0) : 0;
-  p.wl = opts ? opts->window_left : -1;
-  p.wr = opts ? opts->window_right : -1;
+  p.wl = window_side(opts, true);
+  p.wr = window_side(opts, false);
   p.n_ktiles = (int)nkt;
   p.n_qtiles = (int)nqt;
   return launch_status(fa::launch_backward((fa::Dtype)dtype, D, p, (hipStream_t)stream), "varlen backward launch");

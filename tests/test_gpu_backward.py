@@ -278,3 +278,16 @@ def test_backward_full_size_sampled_heads(name, heads):
                       g[b:b + 1, :, hs], sub)
         got = (dq[b:b + 1, :, hs], dk[b:b + 1, :, hk:hk + 1], dv[b:b + 1, :, hk:hk + 1])
         check_grads(got, want, dt, f"{name} b{b} hk{hk}")
+
+
+def test_backward_huge_window_equals_unbounded():
+    print("case backward huge window", flush=True)
+    big = 2 ** 31 - 1
+    q, k, v, g = make(1, 200, 260, 4, 2, 128, torch.bfloat16, seed=4950)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    out, lse = fa.fwd(qd, kd, vd, causal=True)
+    a = fa.bwd(gd, qd, kd, vd, out, lse, causal=True, window_size=(big, big))
+    b = fa.bwd(gd, qd, kd, vd, out, lse, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -593,3 +593,24 @@ def test_prefill_same_bits_for_any_workgroup_rows(opts):
     torch.cuda.synchronize()
     assert torch.equal(small[0][0], large[0][0]) and torch.equal(small[0][0], large[0][127])
     assert torch.equal(small[1][0], large[1][0])
+
+
+def test_huge_window_equals_unbounded():
+    """A window side of 2^31 - 1 reaches every key: the same bits as -1, in the
+    prefill (causal and not) and in the KV-cache decode."""
+    print("case huge window", flush=True)
+    big = 2 ** 31 - 1
+    q, k, v = inputs.dense_qkv(1, 300, 333, 4, 2, 64, torch.float16, seed=4900)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    for causal in (False, True):
+        a = fa.fwd(qd, kd, vd, causal=causal, window_size=(big, big))
+        b = fa.fwd(qd, kd, vd, causal=causal, window_size=(-1, -1))
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    pc = inputs.paged_cache(3, 2, 8, 2, 128, torch.bfloat16, seed=4901, page_size=64, lengths=[300, 5, 129])
+    kv = [t.to(DEV) for t in (pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table)]
+    a = fa.fwd_kvcache(kv[0], kv[1], kv[2], kv[3], block_table=kv[4], num_splits=3, causal=True,
+                       window_size=(big, big))
+    b = fa.fwd_kvcache(kv[0], kv[1], kv[2], kv[3], block_table=kv[4], num_splits=3, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
