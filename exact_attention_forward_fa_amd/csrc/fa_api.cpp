@@ -198,7 +198,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   float scale;
   if ((st = check_opts(opts, D, &scale))) return st;
   if (B == 0 || Sq == 0) return ok();
-  if (!q || !k || !v || !out || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (!q || !out || !lse || (Sk > 0 && (!k || !v))) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FA_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
   const int64_t qd[3] = {(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};
@@ -245,7 +245,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
   float scale;
   if ((st = check_opts(opts, D, &scale))) return st;
   if (B == 0 || Sq == 0) return ok();
-  if (!q || !k || !v || !out || !lse) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (!q || !out || !lse || (Sk > 0 && (!k || !v))) return fail(FA_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FA_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
   const int64_t qd[3] = {(int64_t)Sq * Hq * D, (int64_t)Hq * D, D};

@@ -614,3 +614,16 @@ def test_huge_window_equals_unbounded():
     b = fa.fwd_kvcache(kv[0], kv[1], kv[2], kv[3], block_table=kv[4], num_splits=3, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("D,dt", [(64, torch.float16), (128, torch.bfloat16), (64, torch.float8_e4m3fn)])
+def test_dense_no_keys(D, dt):
+    """Sk = 0: every row has no allowed key, so out = 0 and lse = -inf (k and v
+    may be empty tensors without storage)."""
+    print("case no keys", D, dt, flush=True)
+    q, k, v = inputs.dense_qkv(2, 70, 0, 4, 2, D, torch.float32, seed=4990)
+    qd, kd, vd = (t.to(dt).to(DEV) for t in (q, k, v))
+    out, lse = fa.fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out.float()) == 0
+    assert torch.isneginf(lse).all()
