@@ -157,9 +157,8 @@ void bwd_dkdv_kernel(BackwardParams p) {
   // in contiguous ranges, and within a head the first key tiles (seen by the
   // most queries under a causal mask) go first
   int id = blockIdx.x;
-  if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
-  const int head = id / p.n_ktiles;
-  const int kt = id - head * p.n_ktiles;
+  int head, kt;
+  tile_order(id, (int)(gridDim.x / p.n_ktiles), p.n_ktiles, p.remap_xcd, p.causal, head, kt);   // first key tiles: most queries
   const int b = head / p.Hkv, hk = head - b * p.Hkv;
   int sq = p.Sq, sk = p.Sk, qbase = 0, kbase = 0;
   if (p.cu_seqlens_q) {
@@ -383,9 +382,9 @@ void bwd_dq_kernel(BackwardParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int id = blockIdx.x;
-  if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
-  const int head = id / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);   // last (longest) query tiles first
+  int head, rank;
+  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.causal, head, rank);
+  const int qt = p.n_qtiles - 1 - rank;      // last (longest) query tiles first
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
   int sq = p.Sq, sk = p.Sk, qbase = 0, kbase = 0;
@@ -558,7 +557,7 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
   const int64_t gk = (int64_t)p.n_ktiles * p.B * p.Hkv;
   if (gk > 0) {
     BackwardParams pk = p;
-    pk.remap_xcd = gk % 8 == 0;
+    pk.remap_xcd = ((int64_t)p.B * p.Hkv) % 8 == 0;
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -566,7 +565,7 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
   const int64_t gq = (int64_t)p.n_qtiles * p.B * p.Hq;
   if (gq > 0) {
     BackwardParams pq = p;
-    pq.remap_xcd = gq % 8 == 0;
+    pq.remap_xcd = ((int64_t)p.B * p.Hq) % 8 == 0;
     constexpr int NWQ = bwd_dq_waves<D>();
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, NWQ, SOFTCAP, ALIBI>), dim3((unsigned)gq), dim3(NWQ * 64), 0, s, pq);
     return hipGetLastError();

@@ -226,7 +226,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
   p.block_m = bm;
-  p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
+  p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "prefill launch");
 }
 
@@ -274,7 +274,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
   p.out_scale = v_descale;
   p.n_qtiles = (int)nqt;
   p.block_m = bm;
-  p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
+  p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   return launch_status(fa::launch_prefill_fp8(D, p, (hipStream_t)stream), "fp8 prefill launch");
 }
 
@@ -323,7 +323,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
   p.block_m = bm;
-  p.remap_xcd = ((nqt * Hq * B) % 8) == 0;
+  p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "varlen prefill launch");
 }
 

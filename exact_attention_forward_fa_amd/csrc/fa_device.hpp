@@ -104,6 +104,37 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Workgroup order over (unit, tile) pairs, a unit being a (batch, head) with
+// n_tiles tiles: workgroup id takes the tile of rank `rank` (0 = dispatched
+// first) of unit `unit`.
+//  * rank_major: ranks go slowest, so the tiles of equal rank of every unit are
+//    dispatched together; a caller that maps rank 0 to its longest tile (the
+//    last query tile, or the first key tile, under a causal mask) gets
+//    longest-first over the whole grid.  Unit by unit, the long tiles of the
+//    last units would start late and stretch the tail.
+//  * otherwise units go slowest: the tiles of one unit run together and share
+//    its K/V in L2 (the better order when all tiles are equally long).
+// With xcd set (n_units a multiple of 8), the workgroups the hardware deals to
+// XCD id % 8 cover a contiguous eighth of the units, whose K/V then stay in
+// that XCD's L2.
+__device__ __forceinline__ void tile_order(int id, int n_units, int n_tiles, bool xcd, bool rank_major, int& unit,
+                                           int& rank) {
+  int k = id, u0 = 0, nu = n_units;
+  if (xcd) {
+    nu = n_units >> 3;
+    u0 = (id & 7) * nu;
+    k = id >> 3;
+  }
+  if (rank_major) {
+    rank = k / nu;
+    unit = u0 + (k - rank * nu);
+  } else {
+    const int uu = k / n_tiles;
+    rank = k - uu * n_tiles;
+    unit = u0 + uu;
+  }
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element (i % 4) of the 8-byte chunk addressed by lane
 // 4*j + i/4, for j = 0..3.

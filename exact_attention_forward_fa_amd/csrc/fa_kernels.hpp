@@ -34,7 +34,7 @@ struct PrefillParams {
   int wl, wr;                  // window (left, right), -1 = unbounded
   int n_qtiles;                // ceil(Sq / block_m)
   int block_m;                 // query rows per workgroup (prefill_block_m)
-  int remap_xcd;               // 1 when the grid size is a multiple of 8
+  int remap_xcd;               // 1 when B*Hq is a multiple of 8: each XCD takes a contiguous eighth of the heads
 };
 
 // Split-KV decode over a dense or paged cache: partial results per split.
@@ -125,7 +125,7 @@ struct BackwardParams {
   int wl, wr;
   int n_ktiles;                // ceil(Sk / backward_block_n(D))
   int n_qtiles;                // ceil(Sq / backward_block_m(D))
-  int remap_xcd;               // set per kernel by the launcher
+  int remap_xcd;               // set per kernel by the launcher: its head count is a multiple of 8
 };
 
 hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s);

@@ -97,9 +97,9 @@ void prefill_kernel(PrefillParams p) {
   // 8 XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
   // within a head the longest (last) query tiles go first.
   int id = blockIdx.x;
-  if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
-  const int head = id / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);
+  int head, rank;
+  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.causal, head, rank);
+  const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
 
@@ -498,9 +498,9 @@ void prefill_pp_kernel(PrefillParams p) {
   const int grp = wave >> 2;
 
   int id = blockIdx.x;
-  if (p.remap_xcd) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
-  const int head = id / p.n_qtiles;
-  const int qt = p.n_qtiles - 1 - (id - head * p.n_qtiles);
+  int head, rank;
+  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.causal, head, rank);
+  const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
 
