@@ -753,7 +753,10 @@ template <int D> static int block_m_of(int64_t heads, int max_sq, int cus) {
   if (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128)) return 8 * 32;
   if (S::NW != 8 || S::RB != 1) return S::NW * 32 * S::RB;
   auto wgs = [&](int bm) { return heads * ((max_sq + bm - 1) / bm); };
-  if (wgs(256) >= 2 * (int64_t)cus) return 256;
+  // D = 96: 4-wave workgroups measured faster even on full grids (656 against
+  // 615 TFLOP/s at B=4, S=4096, H=32 causal), 8 waves splitting its 12-piece
+  // rows less evenly
+  if (D != 96 && wgs(256) >= 2 * (int64_t)cus) return 256;
   if (wgs(128) >= (int64_t)cus) return 128;
   return 64;
 }
