@@ -158,7 +158,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
   // most queries under a causal mask) go first
   int id = blockIdx.x;
   int head, kt;
-  tile_order(id, (int)(gridDim.x / p.n_ktiles), p.n_ktiles, p.remap_xcd, p.causal, head, kt);   // first key tiles: most queries
+  tile_order(id, (int)(gridDim.x / p.n_ktiles), p.n_ktiles, p.remap_xcd, p.order_group, head, kt);   // first key tiles: most queries
   const int b = head / p.Hkv, hk = head - b * p.Hkv;
   int sq = p.Sq, sk = p.Sk, qbase = 0, kbase = 0;
   if (p.cu_seqlens_q) {
@@ -383,7 +383,7 @@ void bwd_dq_kernel(BackwardParams p) {
 
   int id = blockIdx.x;
   int head, rank;
-  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.causal, head, rank);
+  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.order_group, head, rank);
   const int qt = p.n_qtiles - 1 - rank;      // last (longest) query tiles first
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
@@ -558,6 +558,7 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
   if (gk > 0) {
     BackwardParams pk = p;
     pk.remap_xcd = ((int64_t)p.B * p.Hkv) % 8 == 0;
+    pk.order_group = order_group(p.causal != 0, (int64_t)p.B * p.Hkv, p.n_ktiles, pk.remap_xcd);
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -566,6 +567,7 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
   if (gq > 0) {
     BackwardParams pq = p;
     pq.remap_xcd = ((int64_t)p.B * p.Hq) % 8 == 0;
+    pq.order_group = order_group(p.causal != 0, (int64_t)p.B * p.Hq, p.n_qtiles, pq.remap_xcd);
     constexpr int NWQ = bwd_dq_waves<D>();
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, NWQ, SOFTCAP, ALIBI>), dim3((unsigned)gq), dim3(NWQ * 64), 0, s, pq);
     return hipGetLastError();

@@ -227,6 +227,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   p.n_qtiles = (int)nqt;
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
+  p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);
   return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "prefill launch");
 }
 
@@ -275,6 +276,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
   p.n_qtiles = (int)nqt;
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
+  p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);
   return launch_status(fa::launch_prefill_fp8(D, p, (hipStream_t)stream), "fp8 prefill launch");
 }
 
@@ -324,6 +326,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   p.n_qtiles = (int)nqt;
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
+  p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);
   return launch_status(fa::launch_prefill((fa::Dtype)dtype, D, p, (hipStream_t)stream), "varlen prefill launch");
 }
 

@@ -107,17 +107,20 @@ __device__ __forceinline__ float sum_xor16(float x) {
 // Workgroup order over (unit, tile) pairs, a unit being a (batch, head) with
 // n_tiles tiles: workgroup id takes the tile of rank `rank` (0 = dispatched
 // first) of unit `unit`.
-//  * rank_major: ranks go slowest, so the tiles of equal rank of every unit are
-//    dispatched together; a caller that maps rank 0 to its longest tile (the
-//    last query tile, or the first key tile, under a causal mask) gets
-//    longest-first over the whole grid.  Unit by unit, the long tiles of the
-//    last units would start late and stretch the tail.
-//  * otherwise units go slowest: the tiles of one unit run together and share
-//    its K/V in L2 (the better order when all tiles are equally long).
+//  * group > 0: the units go in groups of `group`, and inside a group ranks go
+//    slowest, so the tiles of equal rank of the group's units are dispatched
+//    together.  A caller that maps rank 0 to its longest tile (the last query
+//    tile, or the first key tile, under a causal mask) then gets longest-first
+//    within each group; a group that spans at least the workgroups resident on
+//    an XCD keeps the tail short, and a small group keeps few heads' K/V in
+//    flight for the L2.  Unit by unit (group 1), the long tiles of the last
+//    units would start late and stretch the tail.
+//  * group == 0: units go slowest (all tiles of one unit together), the order
+//    for tiles of equal length.
 // With xcd set (n_units a multiple of 8), the workgroups the hardware deals to
 // XCD id % 8 cover a contiguous eighth of the units, whose K/V then stay in
 // that XCD's L2.
-__device__ __forceinline__ void tile_order(int id, int n_units, int n_tiles, bool xcd, bool rank_major, int& unit,
+__device__ __forceinline__ void tile_order(int id, int n_units, int n_tiles, bool xcd, int group, int& unit,
                                            int& rank) {
   int k = id, u0 = 0, nu = n_units;
   if (xcd) {
@@ -125,9 +128,13 @@ __device__ __forceinline__ void tile_order(int id, int n_units, int n_tiles, boo
     u0 = (id & 7) * nu;
     k = id >> 3;
   }
-  if (rank_major) {
-    rank = k / nu;
-    unit = u0 + (k - rank * nu);
+  if (group > 0) {
+    const int per = group * n_tiles;               // workgroups of a full group
+    const int g = k / per;
+    const int gu = min(group, nu - g * group);     // units of this group (the last may have fewer)
+    const int w = k - g * per;
+    rank = w / gu;
+    unit = u0 + g * group + (w - rank * gu);
   } else {
     const int uu = k / n_tiles;
     rank = k - uu * n_tiles;

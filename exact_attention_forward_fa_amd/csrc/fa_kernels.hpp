@@ -35,6 +35,7 @@ struct PrefillParams {
   int n_qtiles;                // ceil(Sq / block_m)
   int block_m;                 // query rows per workgroup (prefill_block_m)
   int remap_xcd;               // 1 when B*Hq is a multiple of 8: each XCD takes a contiguous eighth of the heads
+  int order_group;             // heads per longest-first group (causal), 0 = head by head (see tile_order)
 };
 
 // Split-KV decode over a dense or paged cache: partial results per split.
@@ -126,6 +127,7 @@ struct BackwardParams {
   int n_ktiles;                // ceil(Sk / backward_block_n(D))
   int n_qtiles;                // ceil(Sq / backward_block_m(D))
   int remap_xcd;               // set per kernel by the launcher: its head count is a multiple of 8
+  int order_group;             // set per kernel by the launcher (see tile_order)
 };
 
 hipError_t launch_prefill(Dtype dt, int D, const PrefillParams& p, hipStream_t s);
@@ -157,5 +159,20 @@ int backward_block_m(int D);   // queries per dQ workgroup
 // query rows per prefill workgroup for B*Hq = heads and the longest query
 // sequence, on a device with cus compute units
 int prefill_block_m(int D, int64_t heads, int max_sq, int cus);
+
+// Heads per longest-first group for a grid of n_units heads x n_tiles tiles of
+// unequal length: enough tiles per group to fill the about 64 workgroups an
+// XCD holds at once; 0 (head by head) when the tiles are of equal length.
+inline int order_group(bool unequal, int64_t n_units, int64_t n_tiles, bool xcd) {
+#ifdef FA_ORDER_GROUP
+  return unequal ? FA_ORDER_GROUP : 0;
+#else
+  if (!unequal || n_tiles <= 0) return 0;
+  const int64_t nu = xcd ? n_units / 8 : n_units;
+  int64_t g = (64 + n_tiles - 1) / n_tiles;
+  if (g > nu) g = nu;
+  return g < 1 ? 1 : (int)g;
+#endif
+}
 
 }  // namespace fa

@@ -98,7 +98,7 @@ void prefill_kernel(PrefillParams p) {
   // within a head the longest (last) query tiles go first.
   int id = blockIdx.x;
   int head, rank;
-  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.causal, head, rank);
+  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.order_group, head, rank);
   const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
@@ -499,7 +499,7 @@ void prefill_pp_kernel(PrefillParams p) {
 
   int id = blockIdx.x;
   int head, rank;
-  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.causal, head, rank);
+  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.order_group, head, rank);
   const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
