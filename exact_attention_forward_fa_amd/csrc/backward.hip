@@ -42,11 +42,16 @@ namespace fa {
 //    bank groups (plain operand reads: lane <-> row), and
 //  * rows 4a .. 4a+3 read at the four chunks of one 64-byte column block land on
 //    four distinct 64-byte bank ranges (transposing reads).
+//  (D = 32 and 96: row r starts at bank group 4*(r*D/32 mod 4), so rows
+//  r .. r+3 already fall on distinct 64-byte ranges; XORing the low two chunk
+//  bits with (r/4) mod 4 spreads 16 rows over all 16 groups and keeps every
+//  chunk index below D/8.)
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  static_assert(D == 64 || D == 128, "");
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128, "");
   if constexpr (D == 128) return r * D + 8 * (c ^ (4 * (r & 3) + ((r >> 2) & 3)));
-  else return r * D + 8 * (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
+  else if constexpr (D == 64) return r * D + 8 * (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
+  else return r * D + 8 * (c ^ ((r >> 2) & 3));
 }
 
 // ---------------------------------------------------------------------------
@@ -56,13 +61,15 @@ template <class E, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
-  constexpr int CH = D / 8, RPB = 256 / CH;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CH;   // (b, i, h), h fastest
-  const int c = threadIdx.x % CH;
+  constexpr int CH = D / 8;                                  // 16-byte pieces per row
+  constexpr int CHP = CH <= 4 ? 4 : CH <= 8 ? 8 : 16;        // lanes per row (power of two)
+  constexpr int RPB = 256 / CHP;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CHP;   // (b, i, h), h fastest
+  const int c = threadIdx.x % CHP;
   const int64_t nrows = (int64_t)p.delta_B * p.delta_S * p.Hq;
   float acc = 0.f;
   int64_t b = 0, i = 0, h = 0;
-  if (row < nrows) {
+  if (row < nrows && c < CH) {
     h = row % p.Hq;
     const int64_t bi = row / p.Hq;
     i = bi % p.delta_S;
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
     for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
   }
 #pragma unroll
-  for (int m = CH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  for (int m = CHP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (row < nrows && c == 0) p.delta[b * p.dl_sb + h * p.dl_sh + i] = acc;
 }
 
@@ -134,7 +141,7 @@ constexpr int kBig = 1 << 30;
 // dK, dV: workgroup = NW waves x 32 keys; query tiles of BMQ rows through LDS
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? FA_BWD_KV_WPE128 : FA_BWD_KV_WPE64)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 96 ? FA_BWD_KV_WPE128 : FA_BWD_KV_WPE64)))
 void bwd_dkdv_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -364,7 +371,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
 // dQ: workgroup = NW waves x 32 queries; key tiles of 64 rows through LDS
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 128 ? FA_BWD_Q_WPE128 : FA_BWD_Q_WPE64)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 96 ? FA_BWD_Q_WPE128 : FA_BWD_Q_WPE64)))
 void bwd_dq_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -577,7 +584,8 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
 
 template <class E, int D>
 hipError_t launch_bwd_d(const BackwardParams& p, hipStream_t s) {
-  constexpr int RPB = 256 / (D / 8);
+  constexpr int CH = D / 8;
+  constexpr int RPB = 256 / (CH <= 4 ? 4 : CH <= 8 ? 8 : 16);
   const int64_t rows = (int64_t)p.delta_B * p.delta_S * p.Hq;
   if (rows > 0) {
     hipLaunchKernelGGL((bwd_delta_kernel<E, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
@@ -593,8 +601,12 @@ hipError_t launch_bwd_d(const BackwardParams& p, hipStream_t s) {
 
 template <class E>
 hipError_t launch_bwd_e(int D, const BackwardParams& p, hipStream_t s) {
-  if (D == 64) return launch_bwd_d<E, 64>(p, s);
-  return launch_bwd_d<E, 128>(p, s);
+  switch (D) {
+    case 32: return launch_bwd_d<E, 32>(p, s);
+    case 64: return launch_bwd_d<E, 64>(p, s);
+    case 96: return launch_bwd_d<E, 96>(p, s);
+    default: return launch_bwd_d<E, 128>(p, s);
+  }
 }
 
 hipError_t launch_backward(Dtype dt, int D, const BackwardParams& p, hipStream_t s) {

@@ -213,7 +213,7 @@ size_t fa_bwd_workspace_size(int B, int Sq, int Hq);
  *   dq [B, Sq, Hq, D], dk and dv [B, Sk, Hkv, D] (dtype), contiguous, are
  *   overwritten; GQA kv heads receive the sum over their query heads.  Keys no
  *   query may attend get dk = dv = 0, rows with no allowed key get dq = 0.
- *   opts must be those of the forward call.  D is 64 or 128.
+ *   opts must be those of the forward call.  D is 32, 64, 96 or 128.
  *   workspace: device memory of at least fa_bwd_workspace_size(B, Sq, Hq)
  *   bytes, 16-byte aligned, owned by the caller (NULL allowed when that is 0);
  *   FA_ERR_WORKSPACE_TOO_SMALL otherwise.  Arithmetic: products in fp32 from

@@ -90,6 +90,10 @@ CASES = [
     (1, 1, 1, 2, 2, 64, torch.float16, dict()),
     (1, 1, 70, 2, 1, 128, torch.float16, dict(causal=True)),                   # one query row, decode-like
     (3, 65, 65, 2, 1, 64, torch.bfloat16, dict(causal=True, window=(0, 0))),   # each row sees one key
+    (2, 200, 230, 4, 2, 32, torch.float16, dict(causal=True)),
+    (1, 170, 170, 4, 4, 32, torch.bfloat16, dict(softcap=3.0, alibi_slopes=SLOPES)),
+    (2, 150, 300, 4, 2, 96, torch.bfloat16, dict(causal=True)),
+    (1, 257, 130, 2, 1, 96, torch.float16, dict(causal=True, window=(40, 0), softcap=4.0)),
 ]
 
 
@@ -169,6 +173,8 @@ VARLEN = [
     ([130, 0, 257, 64], [130, 0, 257, 64], 4, 2, 64, torch.float16, dict(causal=True)),
     ([40, 300, 1], [200, 100, 77], 2, 2, 128, torch.bfloat16, dict(causal=True, softcap=3.0)),
     ([96, 33], [96, 0], 4, 1, 64, torch.bfloat16, dict(window=(16, 8), alibi_slopes=SLOPES)),
+    ([70, 200], [70, 200], 2, 2, 32, torch.float16, dict(causal=True)),
+    ([129, 64], [150, 64], 4, 2, 96, torch.bfloat16, dict(causal=True, softcap=2.0)),
 ]
 
 
