@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   const float sl2 = p.scale * kLog2e;
   const float cap_l2 = p.softcap * kLog2e;
   const float cap_in = p.softcap > 0.f ? 2.f * p.scale * kLog2e / p.softcap : 0.f;
-  const int64_t row_elems = (int64_t)p.Hkv * D;
+  const int64_t row_elems = (int64_t)p.kv_heads * D;
   const int page = p.page_size;
   auto div_page = [&](int t) __attribute__((always_inline)) { return p.log2_page >= 0 ? t >> p.log2_page : t / page; };
   auto prow_of = [&](const DecodeChunk& d) __attribute__((always_inline)) {
@@ -257,8 +257,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
                    u32x4 (&qs)[KSTEP], float& sls, auto Swap) __attribute__((always_inline)) {
     constexpr bool swap = decltype(Swap)::value;
     const int b = d.ok ? d.b : 0, hk = d.ok ? d.hk : 0;
-    const T* kh = (const T*)p.k + (int64_t)hk * D;
-    const T* vh = (const T*)p.v + (int64_t)hk * D;
+    const int hc = hk / p.kv_split;                      // the cache head this work head reads
+    const T* kh = (const T*)p.k + (int64_t)hc * D;
+    const T* vh = (const T*)p.v + (int64_t)hc * D;
     int pg0 = 0, e0 = 0, e1 = 0;
     if constexpr (MODE == 1) {
       pg0 = div_page(d.base);
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       const char* vb8 = (const char*)p.v;
       const uint32_t rowb = (uint32_t)(row_elems * sizeof(T));
       const int lr = lane / CHP, c = lcol;
-      const uint32_t lane_off = (uint32_t)hk * (uint32_t)(D * sizeof(T)) + (uint32_t)c * 16u;
+      const uint32_t lane_off = (uint32_t)hc * (uint32_t)(D * sizeof(T)) + (uint32_t)c * 16u;
       const int tl = d.te - 1;
       if constexpr (MODE == 2) {
 #pragma unroll
@@ -523,7 +524,7 @@ static hipError_t launch_dk(const DecodeParams& p, int cus, hipStream_t s) {
 
 template <class E, int D, int MODE>
 static hipError_t launch_dm(const DecodeParams& p, int cus, hipStream_t s) {
-  const int64_t bytes = p.cache_rows * p.Hkv * D * (int64_t)sizeof(typename E::T);
+  const int64_t bytes = p.cache_rows * p.kv_heads * D * (int64_t)sizeof(typename E::T);
   if (bytes <= ((int64_t)1 << 32)) return launch_dk<E, D, MODE, true>(p, cus, s);
   return launch_dk<E, D, MODE, false>(p, cus, s);
 }

@@ -370,9 +370,14 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
     return fail(FA_ERR_INVALID_ARGUMENT, "paged cache needs page_size > 0 and block_table_stride > 0");
   float scale;
   if ((st = check_opts(opts, D, &scale))) return st;
-  if ((Hq / Hkv) * (int64_t)Sq > 16)
-    return fail(FA_ERR_UNSUPPORTED, "(Hq/Hkv)*Sq = %lld query rows per kv head; at most 16 are built",
-                (long long)(Hq / Hkv) * Sq);
+  // the decode works on at most 16 query rows per work item: the query heads of
+  // a kv head are split into kv_split groups (each reading the same K/V) when
+  // (Hq/Hkv)*Sq is larger
+  const int G = Hq / Hkv;
+  int kv_split = 1;
+  while (kv_split <= G && (G % kv_split != 0 || (int64_t)(G / kv_split) * Sq > 16)) ++kv_split;
+  if (kv_split > G)
+    return fail(FA_ERR_UNSUPPORTED, "Sq = %d query positions per kv head; at most 16 are built", Sq);
   if (S_new < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative number of new tokens");
   if (S_new > 0 && (!k_new || !v_new)) return fail(FA_ERR_INVALID_ARGUMENT, "null k_new / v_new");
   const int64_t knd[3] = {(int64_t)S_new * Hkv * D, (int64_t)Hkv * D, D};
@@ -408,9 +413,9 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
     if (workspace_bytes < need)
       return fail(FA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
     // the decode schedule numbers work items (b, split, kv head) and rounds in int
-    if ((int64_t)B * ns * Hkv > (int64_t)1 << 30)
+    if ((int64_t)B * ns * Hkv * kv_split > (int64_t)1 << 30)
       return fail(FA_ERR_UNSUPPORTED, "B*num_splits*Hkv = %lld work items; at most 2^30 are built",
-                  (long long)B * ns * Hkv);
+                  (long long)B * ns * Hkv * kv_split);
   }
 
   hipStream_t s = (hipStream_t)stream;
@@ -458,7 +463,8 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
   }
   d.out_partial = op; d.lse_partial = lp;
   d.order = B > 64 ? order : nullptr;   // up to 64 sequences are ranked inside the decode kernel
-  d.B = B; d.Sq = Sq; d.Hq = Hq; d.Hkv = Hkv; d.group = Hq / Hkv;
+  d.B = B; d.Sq = Sq; d.Hq = Hq; d.Hkv = Hkv * kv_split; d.group = G / kv_split;
+  d.kv_heads = Hkv; d.kv_split = kv_split;
   d.num_splits = ns;
   d.scale = scale;
   d.softcap = opts ? opts->softcap : 0.f;

@@ -54,7 +54,10 @@ struct DecodeParams {
   float* lse_partial;          // [B, Sq, Hq, num_splits] fp32
   int2* order;                 // [B] schedule order: (b, cache_seqlens[b]) by decreasing split length;
                                // nullptr: B <= 64, ranked inside the decode kernel
-  int B, Sq, Hq, Hkv, group;
+  int B, Sq, Hq, Hkv, group;  // Hkv: work heads, kv_heads * kv_split; group = Hq / Hkv query heads each
+  int kv_heads;                // kv heads of the cache
+  int kv_split;                // work heads per cache head: a cache head's query heads split into
+                               // kv_split groups of at most 16 rows, each reading the same K/V
   int num_splits;
   float scale;
   float softcap;

@@ -144,11 +144,15 @@ int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits);
  *     t % page_size (update notes, v2.5).
  *   cache_seqlens: device int32 [B], tokens attended per sequence; the Sq
  *     queries are bottom-right aligned against them.
- *   num_splits: 1..64, or 0 for fa_kvcache_num_splits(); (Hq/Hkv)*Sq <= 16.
+ *   num_splits: 1..64, or 0 for fa_kvcache_num_splits().  Sq <= 16 when each
+ *   kv head has one query head; otherwise any Sq with (Hq/Hkv)*Sq rows that
+ *   can be split over work items of at most 16 rows (the query heads of a kv
+ *   head are split into groups, each group reading the same cache rows);
+ *   FA_ERR_UNSUPPORTED if none.
  *   workspace: device memory of at least fa_kvcache_workspace_size() bytes,
  *     256-byte aligned, any contents; it holds the per-split partials between
  *     the kernels.  Calls sharing a workspace must not overlap in time.
- *   B*num_splits*Hkv <= 2^30.
+ *   B*num_splits*Hkv*(query-head groups per kv head) <= 2^30.
  */
 fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
                          const int* cache_seqlens, const int* block_table, int block_table_stride,

@@ -117,8 +117,8 @@ def test_kvcache_workspace_and_rejects(lib):
     assert kv(ws=ctypes.c_void_p((1 << 20) + 16)) == 2
     assert kv(ns=65) == 2
     assert kv(ns=-1) == 1
-    assert kv(Hq=32, Hkv=1) == 2              # 32 query rows per kv head > 16
-    assert kv(Sq=5) == 2                      # 4 * 5 = 20 rows > 16
+    assert kv(Hq=8, Hkv=8, Sq=17) == 2        # 17 query positions per kv head > 16 (heads split, positions not)
+    assert kv(Hq=32, Hkv=1, Sq=17) == 2
     assert kv(page=0) == 1
     assert lib.fa_fwd_kvcache(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 100, 16, FAKE, 1 << 30, FAKE, FAKE,
                               4, 1, 32, 8, 80, ob, None) == 2   # head dim 80: not built

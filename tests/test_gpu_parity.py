@@ -627,3 +627,38 @@ def test_dense_no_keys(D, dt):
     torch.cuda.synchronize()
     assert torch.count_nonzero(out.float()) == 0
     assert torch.isneginf(lse).all()
+
+
+SPLIT_HEADS = [
+    # (B, Sq, Hq, Hkv, D, dtype, page, lengths, options): (Hq/Hkv)*Sq > 16 query rows per kv head
+    (3, 1, 32, 1, 128, torch.bfloat16, 64, [300, 1, 1000], dict(causal=True)),           # MQA decode
+    (2, 5, 8, 2, 64, torch.float16, 16, [130, 77], dict(causal=True, softcap=5.0)),       # 20 rows
+    (2, 3, 16, 1, 128, torch.float16, 0, [500, 40], dict(causal=True, alibi=True)),       # 48 rows
+    (2, 1, 64, 2, 64, torch.bfloat16, 256, [700, 2000], dict(window=(100, 0))),           # 32 rows
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_HEADS, ids=lambda c: f"B{c[0]}-sq{c[1]}-h{c[2]}/{c[3]}-d{c[4]}-p{c[6]}")
+def test_kvcache_more_than_16_rows_per_kv_head(case):
+    """The query heads of a kv head are split into groups of at most 16 rows
+    that read the same cache; results match the oracle, paged equals dense."""
+    B, Sq, Hq, Hkv, D, dt, page, lens, o = case
+    print("case split heads", case[:7], flush=True)
+    pc = inputs.paged_cache(B, Sq, Hq, Hkv, D, dt, seed=5000 + Hq + Sq, page_size=page or 64, lengths=lens,
+                            tail_fill="nan")
+    slopes = inputs.alibi_slopes(Hq) if o.get("alibi") else None
+    kw = dict(causal=o.get("causal", False), window_size=o.get("window", (-1, -1)), softcap=o.get("softcap", 0.0),
+              alibi_slopes=None if slopes is None else slopes.to(DEV))
+    kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
+    vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
+    dense = fa.fwd_kvcache(pc.q.to(DEV), kd.to(DEV), vd.to(DEV), pc.cache_seqlens.to(DEV), num_splits=3, **kw)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, page or 64,
+                                   causal=kw["causal"], window=kw["window_size"], softcap=kw["softcap"],
+                                   alibi_slopes=slopes)
+    check(dense[0].cpu(), dense[1].cpu(), ro, rl, dt, f"split heads dense {case[:7]}")
+    if page:
+        paged = fa.fwd_kvcache(pc.q.to(DEV), pc.k_pool.to(DEV), pc.v_pool.to(DEV), pc.cache_seqlens.to(DEV),
+                               block_table=pc.block_table.to(DEV), num_splits=3, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(paged[0], dense[0]) and torch.equal(paged[1], dense[1])
