@@ -293,7 +293,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   float scale;
   if ((st = check_opts(opts, D, &scale))) return st;
   if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ok();
-  if (!q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k)
+  if (!q || !out || !lse || !cu_seqlens_q || !cu_seqlens_k || (total_k > 0 && (!k || !v)))
     return fail(FA_ERR_INVALID_ARGUMENT, "null pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(FA_ERR_UNSUPPORTED, "q/k/v/out must be 16-byte aligned");
