@@ -29,6 +29,7 @@
 //  * an item's token range is clamped to the union of its rows' sliding windows,
 //    so keys no row can see are never read.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
@@ -508,13 +509,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
 
 template <class E, int D, int MODE, bool OFF32>
 static hipError_t launch_dk(const DecodeParams& p, int cus, hipStream_t s) {
-  static int per_cu = 0;   // resident workgroups per CU (the same on every gfx950 device)
+  // resident workgroups per CU (the same on every gfx950 device); computed once,
+  // and a concurrent first call at worst computes the same value twice
+  static std::atomic<int> cached{0};
+  int per_cu = cached.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<E, D, MODE, OFF32>, 64, 0) != hipSuccess ||
         nb < 1)
       nb = 1;
     per_cu = nb;
+    cached.store(nb, std::memory_order_relaxed);
   }
   const int64_t items = (int64_t)p.B * p.num_splits * p.Hkv;
   const int grid = (int)std::min<int64_t>(items, (int64_t)cus * per_cu);
