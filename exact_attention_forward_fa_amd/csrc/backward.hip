@@ -48,8 +48,8 @@ namespace fa {
 //  chunk index below D/8.)
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  static_assert(D == 32 || D == 64 || D == 96 || D == 128, "");
-  if constexpr (D == 128) return r * D + 8 * (c ^ (4 * (r & 3) + ((r >> 2) & 3)));
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "");
+  if constexpr (D >= 128) return r * D + 8 * (c ^ (4 * (r & 3) + ((r >> 2) & 3)));
   else if constexpr (D == 64) return r * D + 8 * (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
   else return r * D + 8 * (c ^ ((r >> 2) & 3));
 }
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
   constexpr int CH = D / 8;                                  // 16-byte pieces per row
-  constexpr int CHP = CH <= 4 ? 4 : CH <= 8 ? 8 : 16;        // lanes per row (power of two)
+  constexpr int CHP = CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32;   // lanes per row (power of two)
   constexpr int RPB = 256 / CHP;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CHP;   // (b, i, h), h fastest
   const int c = threadIdx.x % CHP;
@@ -138,15 +138,20 @@ constexpr int kBig = 1 << 30;
 #endif
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = NW waves x 32 keys; query tiles of BMQ rows through LDS
+// dK, dV: workgroup = NW waves x 32 keys; query tiles of BMQ rows through LDS.
+// PART 0 accumulates both; at D = 256, where K, V, dK and dV of 32 keys do not
+// fit one wave's registers, PART 1 accumulates dV only (S, then P^T dO) and
+// PART 2 dK only (S, dP, then dS^T Q), in two launches; PART 2 keeps the V rows
+// in LDS instead of registers (each lane reads back only what it wrote).
 // ---------------------------------------------------------------------------
-template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
+template <class E, int D, int NW, bool SOFTCAP, bool ALIBI, int PART>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 96 ? FA_BWD_KV_WPE128 : FA_BWD_KV_WPE64)))
 void bwd_dkdv_kernel(BackwardParams p) {
+  constexpr bool DO_DV = PART != 2, DO_DK = PART != 1, V_LDS = PART == 2;
   using T = typename E::T;
   using V8 = typename E::V8;
   using V2 = typename E::V2;
-  constexpr int BMQ = D >= 128 ? FA_BWD_KV_BMQ128 : FA_BWD_KV_BMQ64;   // query rows per LDS tile
+  constexpr int BMQ = V_LDS ? 32 : D >= 128 ? FA_BWD_KV_BMQ128 : FA_BWD_KV_BMQ64;   // query rows per LDS tile
   constexpr int BNK = NW * 32;            // keys per workgroup
   constexpr int CH = D / 8, DC = D / 16, DB = D / 32;
   constexpr int NT = NW * 64;
@@ -156,6 +161,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) T gsm[2][BMQ * D];     // dO
   __shared__ __attribute__((aligned(16))) float lsm[2][BMQ];     // lse in log2 units; +inf: row adds nothing
   __shared__ __attribute__((aligned(16))) float esm[2][BMQ];     // delta
+  __shared__ __attribute__((aligned(16))) T vsm[V_LDS ? NW * 32 * D : 8];   // V rows of each wave's keys
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -198,14 +204,16 @@ void bwd_dkdv_kernel(BackwardParams p) {
 
   // K and V rows of the lane's key: B operands of S = Q Kᵀ and dP = dO Vᵀ
   // (lane <-> key, d = 16dc + 8hi .. +7)
-  V8 kr[DC], vr[DC];
+  V8 kr[DC], vr[DO_DK && !V_LDS ? DC : 1];
+  T* const vw = vsm + (V_LDS ? wave * 32 * D : 0);   // the wave's V rows (V_LDS)
   {
     const T* kp = (const T*)p.k + bq * p.k_sb + (int64_t)(kbase + jc) * p.k_ss + (int64_t)hk * p.k_sh + hi * 8;
     const T* vp = (const T*)p.v + bq * p.v_sb + (int64_t)(kbase + jc) * p.v_ss + (int64_t)hk * p.v_sh + hi * 8;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       kr[dc] = *(const V8*)(kp + dc * 16);
-      vr[dc] = *(const V8*)(vp + dc * 16);
+      if constexpr (V_LDS) *(V8*)(vw + swz<D>(l32, 2 * dc + hi)) = *(const V8*)(vp + dc * 16);
+      else if constexpr (DO_DK) vr[dc] = *(const V8*)(vp + dc * 16);
     }
   }
   const float sl2 = p.scale * kLog2e;
@@ -251,11 +259,11 @@ void bwd_dkdv_kernel(BackwardParams p) {
     }
   };
 
-  f32x16 dk[DB], dv[DB];
+  f32x16 dk[DO_DK ? DB : 1], dv[DO_DV ? DB : 1];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
+    if constexpr (DO_DK) dk[db] = f32x16{};
+    if constexpr (DO_DV) dv[db] = f32x16{};
   }
 
   // transposing-read addressing: lane (4a + g) of each 16-lane group reads row
@@ -273,7 +281,8 @@ void bwd_dkdv_kernel(BackwardParams p) {
     for (int dc = 0; dc < DC; ++dc) {
       const int off = swz<D>(rb0 + l32, 2 * dc + hi);
       s = E::mfma32(*(const V8*)(qs + off), kr[dc], s);
-      dp = E::mfma32(*(const V8*)(gs + off), vr[dc], dp);
+      if constexpr (V_LDS) dp = E::mfma32(*(const V8*)(gs + off), *(const V8*)(vw + swz<D>(l32, 2 * dc + hi)), dp);
+      else if constexpr (DO_DK) dp = E::mfma32(*(const V8*)(gs + off), vr[dc], dp);
     }
     // register r of s holds query row rb0 + 8(r/4) + 4hi + r%4 for the lane's key
     f32x4 L[4], Dl[4];
@@ -299,7 +308,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
           if (i < a_j || i > b_j) pv = 0.f;
         }
         pr[u] = pv;
-        ds[u] = pv * (dp[rr] - Dl[rr >> 2][rr & 3]) * dcap;
+        ds[u] = DO_DK ? pv * (dp[rr] - Dl[rr >> 2][rr & 3]) * dcap : 0.f;
       }
       const V2 pp = E::pack(pr[0], pr[1]);
       const V2 sp = E::pack(ds[0], ds[1]);
@@ -317,12 +326,16 @@ void bwd_dkdv_kernel(BackwardParams p) {
       for (int db = 0; db < DB; ++db) {
         const int o1 = swz<D>(r1, 4 * db + tr_chunk) + tr_elem;
         const int o2 = swz<D>(r2, 4 * db + tr_chunk) + tr_elem;
-        const i16x4 g0 = lds_read_tr16(gs + o1), g1 = lds_read_tr16(gs + o2);
-        const i16x4 q0 = lds_read_tr16(qs + o1), q1 = lds_read_tr16(qs + o2);
-        const V8 gb = __builtin_bit_cast(V8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
-        const V8 qb = __builtin_bit_cast(V8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
-        dv[db] = E::mfma32(pa[c2], gb, dv[db]);
-        dk[db] = E::mfma32(sa[c2], qb, dk[db]);
+        if constexpr (DO_DV) {
+          const i16x4 g0 = lds_read_tr16(gs + o1), g1 = lds_read_tr16(gs + o2);
+          const V8 gb = __builtin_bit_cast(V8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dv[db] = E::mfma32(pa[c2], gb, dv[db]);
+        }
+        if constexpr (DO_DK) {
+          const i16x4 q0 = lds_read_tr16(qs + o1), q1 = lds_read_tr16(qs + o2);
+          const V8 qb = __builtin_bit_cast(V8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+          dk[db] = E::mfma32(sa[c2], qb, dk[db]);
+        }
       }
     }
   };
@@ -360,23 +373,26 @@ void bwd_dkdv_kernel(BackwardParams p) {
     if (key < sk) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dkp[(int64_t)key * p.dk_ss + db * 32 + l32] = E::from_f32(dk[db][r] * p.scale);
-        dvp[(int64_t)key * p.dv_ss + db * 32 + l32] = E::from_f32(dv[db][r]);
+        if constexpr (DO_DK) dkp[(int64_t)key * p.dk_ss + db * 32 + l32] = E::from_f32(dk[db][r] * p.scale);
+        if constexpr (DO_DV) dvp[(int64_t)key * p.dv_ss + db * 32 + l32] = E::from_f32(dv[db][r]);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = NW waves x 32 queries; key tiles of 64 rows through LDS
+// dQ: workgroup = NW waves x 32 queries; key tiles of BN rows through LDS.  At
+// D = 256 the dO rows of each wave's queries sit in LDS instead of registers
+// (each lane reads back only what it wrote), so that Q, dQ and the products fit.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, bool SOFTCAP, bool ALIBI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 96 ? FA_BWD_Q_WPE128 : FA_BWD_Q_WPE64)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : D >= 96 ? FA_BWD_Q_WPE128 : FA_BWD_Q_WPE64)))
 void bwd_dq_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
   using V2 = typename E::V2;
-  constexpr int BN = 64;                  // keys per LDS tile
+  constexpr bool G_LDS = D >= 256;
+  constexpr int BN = D >= 256 ? 32 : 64;  // keys per LDS tile
   constexpr int BM = NW * 32;             // queries per workgroup
   constexpr int CH = D / 8, DC = D / 16, DB = D / 32;
   constexpr int NT = NW * 64;
@@ -384,6 +400,7 @@ void bwd_dq_kernel(BackwardParams p) {
   static_assert(LK * NT == BN * CH, "");
   __shared__ __attribute__((aligned(16))) T ksm[2][BN * D];
   __shared__ __attribute__((aligned(16))) T vsm[2][BN * D];
+  __shared__ __attribute__((aligned(16))) T gsm[G_LDS ? NW * 32 * D : 8];   // dO rows of each wave's queries
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -425,14 +442,16 @@ void bwd_dq_kernel(BackwardParams p) {
   const int t_hi = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : t_lo;
 
   // Q and dO rows of the lane's query: B operands of Sᵀ = K Qᵀ and dPᵀ = V dOᵀ
-  V8 qr[DC], gr[DC];
+  V8 qr[DC], gr[G_LDS ? 1 : DC];
+  T* const gw = gsm + (G_LDS ? wave * 32 * D : 0);   // the wave's dO rows (G_LDS)
   {
     const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)(qbase + ic) * p.q_ss + (int64_t)hq * p.q_sh + hi * 8;
     const T* gp = (const T*)p.dout + bq * p.do_sb + (int64_t)(qbase + ic) * p.do_ss + (int64_t)hq * p.do_sh + hi * 8;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       qr[dc] = *(const V8*)(qp + dc * 16);
-      gr[dc] = *(const V8*)(gp + dc * 16);
+      if constexpr (G_LDS) *(V8*)(gw + swz<D>(l32, 2 * dc + hi)) = *(const V8*)(gp + dc * 16);
+      else gr[dc] = *(const V8*)(gp + dc * 16);
     }
   }
   const float lse = p.lse[bq * p.lse_sb + (int64_t)hq * p.lse_sh + qbase + ic];
@@ -478,7 +497,8 @@ void bwd_dq_kernel(BackwardParams p) {
     for (int dc = 0; dc < DC; ++dc) {
       const int off = swz<D>(kb0 + l32, 2 * dc + hi);
       s = E::mfma32(*(const V8*)(ks + off), qr[dc], s);
-      dp = E::mfma32(*(const V8*)(vs + off), gr[dc], dp);
+      if constexpr (G_LDS) dp = E::mfma32(*(const V8*)(vs + off), *(const V8*)(gw + swz<D>(l32, 2 * dc + hi)), dp);
+      else dp = E::mfma32(*(const V8*)(vs + off), gr[dc], dp);
     }
     // register r holds key j0 + 8(r/4) + 4hi + r%4 for the lane's query
     V8 sa[2];
@@ -553,10 +573,10 @@ void bwd_dq_kernel(BackwardParams p) {
 // host launchers
 // ---------------------------------------------------------------------------
 template <int D> constexpr int bwd_dkdv_waves() { return D >= 128 ? FA_BWD_KV_NW128 : FA_BWD_KV_NW64; }
-template <int D> constexpr int bwd_dq_waves() { return D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64; }
+template <int D> constexpr int bwd_dq_waves() { return D >= 256 ? 4 : D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64; }
 
 int backward_block_n(int D) { return (D >= 128 ? FA_BWD_KV_NW128 : FA_BWD_KV_NW64) * 32; }
-int backward_block_m(int D) { return (D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64) * 32; }
+int backward_block_m(int D) { return (D >= 256 ? 4 : D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64) * 32; }
 
 template <class E, int D, bool SOFTCAP, bool ALIBI>
 hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
@@ -566,7 +586,14 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
     BackwardParams pk = p;
     pk.remap_xcd = ((int64_t)p.B * p.Hkv) % 8 == 0;
     pk.order_group = order_group(p.causal != 0, (int64_t)p.B * p.Hkv, p.n_ktiles, pk.remap_xcd);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
+    if constexpr (D >= 256) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI, 1>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI, 2>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI, 0>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -585,7 +612,7 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
 template <class E, int D>
 hipError_t launch_bwd_d(const BackwardParams& p, hipStream_t s) {
   constexpr int CH = D / 8;
-  constexpr int RPB = 256 / (CH <= 4 ? 4 : CH <= 8 ? 8 : 16);
+  constexpr int RPB = 256 / (CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32);
   const int64_t rows = (int64_t)p.delta_B * p.delta_S * p.Hq;
   if (rows > 0) {
     hipLaunchKernelGGL((bwd_delta_kernel<E, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
@@ -605,6 +632,7 @@ hipError_t launch_bwd_e(int D, const BackwardParams& p, hipStream_t s) {
     case 32: return launch_bwd_d<E, 32>(p, s);
     case 64: return launch_bwd_d<E, 64>(p, s);
     case 96: return launch_bwd_d<E, 96>(p, s);
+    case 256: return launch_bwd_d<E, 256>(p, s);
     default: return launch_bwd_d<E, 128>(p, s);
   }
 }

@@ -523,7 +523,6 @@ fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k,
                  void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(dtype, Hq, Hkv, D);
   if (st) return st;
-  if (D == 256) return fail(FA_ERR_UNSUPPORTED, "backward head_dim %d not built (32, 64, 96 or 128)", D);
   if (B < 0 || Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size (B=%d Sq=%d Sk=%d)", B, Sq, Sk);
   float scale;
   if ((st = check_opts(opts, D, &scale))) return st;
@@ -593,7 +592,6 @@ fa_status fa_bwd_varlen(fa_dtype dtype, const void* dout, const void* q, const v
                         void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(dtype, Hq, Hkv, D);
   if (st) return st;
-  if (D == 256) return fail(FA_ERR_UNSUPPORTED, "backward head_dim %d not built (32, 64, 96 or 128)", D);
   if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
   float scale;

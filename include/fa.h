@@ -18,8 +18,8 @@
  *  - Element type: fa_dtype (fp16 or bf16) for q/k/v/out; float32 for lse,
  *    ALiBi slopes and the decode workspace; int32 for cu_seqlens,
  *    cache_seqlens and block_table.
- *  - Head dimension D: 32, 64, 96, 128 or 256 for fa_fwd, fa_fwd_varlen and the
- *    KV-cache calls; any D for fa_combine.  Other values return
+ *  - Head dimension D: 32, 64, 96, 128 or 256 for fa_fwd, fa_fwd_varlen, the
+ *    KV-cache calls, fa_bwd and fa_bwd_varlen; any D for fa_combine.  Other values return
  *    FA_ERR_UNSUPPORTED.  The head-dim stride is 1 and row starts must be
  *    16-byte aligned (strides multiples of 8 elements, base pointers 16-byte
  *    aligned).
@@ -217,7 +217,7 @@ size_t fa_bwd_workspace_size(int B, int Sq, int Hq);
  *   dq [B, Sq, Hq, D], dk and dv [B, Sk, Hkv, D] (dtype), contiguous, are
  *   overwritten; GQA kv heads receive the sum over their query heads.  Keys no
  *   query may attend get dk = dv = 0, rows with no allowed key get dq = 0.
- *   opts must be those of the forward call.  D is 32, 64, 96 or 128.
+ *   opts must be those of the forward call.  D is 32, 64, 96, 128 or 256.
  *   workspace: device memory of at least fa_bwd_workspace_size(B, Sq, Hq)
  *   bytes, 16-byte aligned, owned by the caller (NULL allowed when that is 0);
  *   FA_ERR_WORKSPACE_TOO_SMALL otherwise.  Arithmetic: products in fp32 from

@@ -180,7 +180,7 @@ def test_bwd_rejects(lib):
         return lib.fa_bwd(dtype, *p, B, Sq, Sk, Hq, Hkv, D, *s, o if o is not None else ob, ws, wsb, None)
     assert bw(dtype=3) == 1
     assert bw(Hq=3, Hkv=2) == 1
-    assert bw(D=256) == 2                     # backward: D 32, 64, 96 or 128
+    assert bw(D=48) == 2                      # D 32, 64, 96, 128 or 256
     assert bw(D=80) == 2
     assert bw(Sq=-1) == 1
     assert bw(wsb=100) == 3                   # 2*2*8*4 = 128 -> 256 bytes needed
@@ -209,7 +209,7 @@ def test_bwd_varlen_rejects(lib):
         p = ptrs or [FAKE] * 9
         return lib.fa_bwd_varlen(0, *p, cu, cu, B, mq, mk, tq, tk, 2, 2, D, None, None, None, None, None, ob,
                                  ws, wsb, None)
-    assert bv(D=256) == 2
+    assert bv(D=80) == 2
     assert bv(tq=-1) == 1
     assert bv(cu=None) == 1
     assert bv(wsb=16) == 3                    # 2 heads * 12 rows * 4 bytes -> 256 needed

@@ -94,6 +94,10 @@ CASES = [
     (1, 170, 170, 4, 4, 32, torch.bfloat16, dict(softcap=3.0, alibi_slopes=SLOPES)),
     (2, 150, 300, 4, 2, 96, torch.bfloat16, dict(causal=True)),
     (1, 257, 130, 2, 1, 96, torch.float16, dict(causal=True, window=(40, 0), softcap=4.0)),
+    (1, 300, 300, 2, 1, 256, torch.bfloat16, dict(causal=True)),
+    (2, 150, 270, 4, 2, 256, torch.float16, dict(window=(40, 20), softcap=3.0)),
+    (1, 257, 130, 2, 2, 256, torch.float16, dict(causal=True, alibi_slopes=SLOPES)),   # rows with no allowed key
+    (1, 1, 70, 2, 1, 256, torch.bfloat16, dict()),
 ]
 
 
@@ -175,6 +179,7 @@ VARLEN = [
     ([96, 33], [96, 0], 4, 1, 64, torch.bfloat16, dict(window=(16, 8), alibi_slopes=SLOPES)),
     ([70, 200], [70, 200], 2, 2, 32, torch.float16, dict(causal=True)),
     ([129, 64], [150, 64], 4, 2, 96, torch.bfloat16, dict(causal=True, softcap=2.0)),
+    ([150, 0, 40], [150, 30, 170], 2, 1, 256, torch.float16, dict(causal=True, window=(60, 0))),
 ]
 
 

@@ -62,8 +62,6 @@ def test_random_dense_forward_and_backward(seed):
     torch.cuda.synchronize()
     ro, rl = ref.attention(q, k, v, **oracle_kw(c, slopes))
     check(out.cpu(), lse.cpu(), ro, rl, c["dt"], f"random fwd {seed}")
-    if c["D"] == 256:
-        return
     g = inputs.randn(torch.Generator().manual_seed(7200 + seed), q.shape, c["dt"])
     dq, dk, dv = fa.bwd(g.to(DEV), qd, kd, vd, out, lse, alibi_slopes=sd, **kw)
     torch.cuda.synchronize()
