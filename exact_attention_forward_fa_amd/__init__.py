@@ -355,7 +355,7 @@ def bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(
         alibi_slopes=None, dq=None, dk=None, dv=None, workspace=None, deterministic=True):
     """Gradients of ``fwd``: returns (dq [B,Sq,Hq,D], dk, dv [B,Sk,Hkv,D]) for the
     gradient ``dout`` of ``out``.  ``out`` and ``lse`` are what ``fwd`` returned
-    for the same q, k, v and options.  D is 32, 64, 96 or 128.  The kernels are
+    for the same q, k, v and options.  D is 32, 64, 96, 128 or 256.  The kernels are
     deterministic (``deterministic`` is accepted for interface parity)."""
     _need_gpu(dout, q, k, v, out, lse)
     if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in (k, v, out, dout)):

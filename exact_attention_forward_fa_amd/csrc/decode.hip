@@ -161,7 +161,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     }
     s_ord[rank] = make_int2(lane, lb);
   }
-  auto item_of = [&](int r) __attribute__((always_inline)) { return r * P + ((r & 1) ? P - 1 - w : w); };
+  // A kv head's row that does not fill whole 128-byte lines (D = 32: 64 bytes,
+  // D = 96: 192) shares lines with the neighbouring heads of the same token.
+  // Workgroup w runs on XCD w mod 8, so there the slots of a round are dealt so
+  // that each XCD's workgroups take 8 consecutive slots (the heads of one
+  // sequence and split) and the shared lines are fetched into one L2.  The
+  // snake pairing is kept: a workgroup takes slot ws in even rounds and
+  // P - 1 - ws in odd ones.
+  constexpr bool kGroupHeads = (D * sizeof(T)) % 128 != 0;
+  const int ws = !kGroupHeads || w >= (P & ~63) ? w : (w & ~63) + 8 * (w & 7) + ((w >> 3) & 7);
+  auto item_of = [&](int r) __attribute__((always_inline)) { return r * P + ((r & 1) ? P - 1 - ws : ws); };
   int rb = 0, lr = -1;
   auto load_window = [&]() __attribute__((always_inline)) {
     const int k = item_of(rb + lane);

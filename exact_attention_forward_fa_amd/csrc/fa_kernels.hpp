@@ -140,7 +140,7 @@ int prefill_block_m_fp8(int D);
 hipError_t launch_decode(Dtype dt, int D, const DecodeParams& p, hipStream_t s);
 hipError_t launch_combine(Dtype dt, const CombineParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
-// D in {64, 128}; launches nothing for an empty grid
+// D in {32, 64, 96, 128, 256}; launches nothing for an empty grid
 hipError_t launch_backward(Dtype dt, int D, const BackwardParams& p, hipStream_t s);
 int backward_block_n(int D);   // keys per dK/dV workgroup
 int backward_block_m(int D);   // queries per dQ workgroup

@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, Hq % Hkv != 0, window < -1, ... */
-  FA_ERR_UNSUPPORTED = 2,        /* valid but not built: D not in {64,128}, misalignment, ... */
+  FA_ERR_UNSUPPORTED = 2,        /* valid but not built: D not in {32,64,96,128,256}, misalignment, ... */
   FA_ERR_WORKSPACE_TOO_SMALL = 3,/* decode workspace below fa_kvcache_workspace_size() */
   FA_ERR_HIP = 4                 /* a HIP launch error; fa_last_error() carries its text */
 } fa_status;
