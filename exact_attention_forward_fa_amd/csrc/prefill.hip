@@ -60,7 +60,7 @@ template <int D> constexpr int k_stride() { return D + 8; }
 template <int D> constexpr int v_stride() { return D + (D == 96 ? 0 : D == 32 ? 64 : FA_PREFILL_VPAD); }
 
 template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI, bool F8 = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 || (NW <= 2 && D >= 96) ? 1 : D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -393,8 +393,22 @@ void prefill_kernel(PrefillParams p) {
     // Transposing read: lane (g = lane % 16) of each 16-lane group addresses row
     // 16c + 4hi + g/4 (+8 for the second half), columns 32db + 16((lane/16)%2) + 4(g%4).
     const T* vbase = Vs + (hi * 4 + ((lane & 15) >> 2)) * VS + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    // the V operands of two 16-key chunks are read ahead of their MFMAs (all
+    // four chunks at once do not fit the register budget)
+    V8 vop[BN / 16][DB];
 #pragma unroll
     for (int c = 0; c < BN / 16; ++c) {
+      if ((c & 1) == 0) {
+#pragma unroll
+        for (int cc = c; cc < c + 2 && cc < BN / 16; ++cc)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const i16x4 x0 = lds_read_tr16(vbase + cc * 16 * VS + db * 32);
+            const i16x4 x1 = lds_read_tr16(vbase + (cc * 16 + 8) * VS + db * 32);
+            vop[cc][db] = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int kb = c >> 1, c2 = c & 1;
       V8 bop[RB];
 #pragma unroll
@@ -406,11 +420,8 @@ void prefill_kernel(PrefillParams p) {
         }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const i16x4 x0 = lds_read_tr16(vbase + c * 16 * VS + db * 32);
-        const i16x4 x1 = lds_read_tr16(vbase + (c * 16 + 8) * VS + db * 32);
-        const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mfma32(a, bop[rb], o[rb][db]);
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mfma32(vop[c][db], bop[rb], o[rb][db]);
       }
     }
   };
