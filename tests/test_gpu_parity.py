@@ -579,6 +579,21 @@ def test_fp8_prefill(case):
     check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"fp8 {case}")
 
 
+def test_fp8_prefill_full_size_sampled_rows():
+    """The fp8 prefill at the size and in the launch configuration the benchmark
+    times (B=4, S=4096, H=32, D=64 causal, the fp16 inputs converted to e4m3,
+    descales 1), checked on sampled rows against the oracle on the e4m3 values."""
+    print("case fp8 c3_causal", flush=True)
+    c = inputs.case("c3_causal")
+    q8, k8, v8 = (c[x].to(torch.float8_e4m3fn) for x in ("q", "k", "v"))
+    out, lse = fa.fwd(q8.to(DEV), k8.to(DEV), v8.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    rows = _sample_rows(q8.shape[1], 9)
+    ro, rl = ref.attention(q8.double(), k8.double(), v8.double(), causal=True, rows=rows)
+    check(out.cpu()[:, rows], lse.cpu()[:, :, rows], ro, rl, torch.bfloat16, "fp8 c3_causal")
+
+
 @pytest.mark.parametrize("opts", [dict(causal=True), dict(window=(100, 20)), dict(causal=True, softcap=8.0)])
 def test_prefill_same_bits_for_any_workgroup_rows(opts):
     """A small grid runs 64-row workgroups and a large one 256-row workgroups; each
