@@ -130,6 +130,27 @@ def test_c5_paged_decode_full(c5):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+def test_c5_decode_with_one_token_append(c5):
+    """Config 5 in the form the benchmark times with an append: each sequence's
+    last token is written again from k=, v= (its own values) at position
+    cache_seqlens - 1 and attended with the rest.  The pool must be unchanged and
+    the result equal, bit for bit, the plain decode of the full cache."""
+    print("case c5_append", flush=True)
+    page = c5["page_size"]
+    last = c5["cache_seqlens"].long() - 1
+    pages = c5["block_table"][torch.arange(last.numel()), last // page].long()
+    kn = c5["k_pool"][pages, last % page].unsqueeze(1).contiguous()
+    vn = c5["v_pool"][pages, last % page].unsqueeze(1).contiguous()
+    kp, vp = c5["k_pool"].to(DEV), c5["v_pool"].to(DEV)
+    out, lse = fa.fwd_kvcache(c5["q"].to(DEV), kp, vp, (c5["cache_seqlens"] - 1).to(DEV),
+                              block_table=c5["block_table"].to(DEV), num_splits=c5.get("num_splits", 0),
+                              k=kn.to(DEV), v=vn.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(kp.cpu(), c5["k_pool"]) and torch.equal(vp.cpu(), c5["v_pool"])
+    ro, rl = run_paged(c5)
+    assert torch.equal(out.cpu(), ro) and torch.equal(lse.cpu(), rl)
+
+
 def test_c5_paged_equals_dense_cache_bitexact(c5):
     kd = inputs.dense_cache_from_pool(c5["k_pool"], c5["block_table"], c5["cache_seqlens"])
     vd = inputs.dense_cache_from_pool(c5["v_pool"], c5["block_table"], c5["cache_seqlens"])
