@@ -143,7 +143,7 @@ def main():
                     help="after timing, run one device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
