@@ -132,6 +132,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   const int rows = p.group * p.Sq;
   const int sqi = n / p.group, gq = n - sqi * p.group;   // row n: position sqi, head hk*G + gq
   const bool live = n < rows;
+  // several cache heads per work head: row n's query head belongs to cache head
+  // hrow of the work head, whose elements are D-row elements hrow*head_dim ..
+  const int heads_per_item = p.head_shift < 30 ? D >> p.head_shift : 1;
+  const int hrow = gq / (p.group / heads_per_item);
   const float sl2 = p.scale * kLog2e;
   const float cap_l2 = p.softcap * kLog2e;
   const float cap_in = p.softcap > 0.f ? 2.f * p.scale * kLog2e / p.softcap : 0.f;
@@ -341,9 +345,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       }
     }
     const int hq = hk * p.group + (live ? gq : 0);
-    const T* qrow = (const T*)p.q + (((int64_t)b * p.Sq + (live ? sqi : 0)) * p.Hq + hq) * D + q4 * 8;
+    // q holds at most 2^31 bytes (checked on the host): a 32-bit byte offset per
+    // lane from a wave-uniform base, the piece's place within its head uniform per ks
+    const uint32_t qoff = (uint32_t)(((b * p.Sq + (live ? sqi : 0)) * p.Hq + hq) * p.head_dim + q4 * 8) *
+                          (uint32_t)sizeof(T);
+    const int qmask = (1 << p.head_shift) - 1;   // element within its head (all ones: one head)
 #pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) qs[ks] = *(const u32x4*)(qrow + ks * 32);
+    for (int ks = 0; ks < KSTEP; ++ks)
+      qs[ks] = *(const u32x4*)((const char*)p.q + ((ks * 32) & qmask) * (int)sizeof(T) + qoff);
     sls = *(p.alibi ? p.alibi + hq : p.lse_partial);
   };
   // ---- per-item row state.  Row n sees tokens [rlo, rhi] of the item; every
@@ -354,8 +363,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   int rlo = 0, rhi = -1, wlo = 0, whi = -1;
 
   auto begin_item = [&](const DecodeChunk& d, const u32x4 (&qs)[KSTEP], float sls) __attribute__((always_inline)) {
+    // the row's query sits in its own cache head's elements, zeros elsewhere, so
+    // the scores take only that head's keys
 #pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) qb[ks] = __builtin_bit_cast(V8, live ? qs[ks] : u32x4{});
+    for (int ks = 0; ks < KSTEP; ++ks)
+      qb[ks] = __builtin_bit_cast(V8, live && ((ks * 32 + q4 * 8) >> p.head_shift) == hrow ? qs[ks] : u32x4{});
     slope = (p.alibi && live) ? sls * kLog2e : 0.f;
     const int ip = sqi + d.len - p.Sq;     // bottom-right aligned position of the row
     ipf = (float)ip;
@@ -468,9 +480,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       if (live) {
         const int64_t prow = prow_of(d);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        float* dst = p.out_partial + prow * D;
+        // only the row's own cache head's elements of O are its output
+        float* dst = p.out_partial + prow * p.head_dim + 4 * q4;
 #pragma unroll
-        for (int db = 0; db < DBK; ++db) *(f32x4*)(dst + db * 16 + 4 * q4) = o[db] * inv;
+        for (int db = 0; db < DBK; ++db)
+          if (((db * 16) >> p.head_shift) == hrow) *(f32x4*)(dst + db * 16 - hrow * p.head_dim) = o[db] * inv;
         if (q4 == 0) p.lse_partial[prow] = lxt > 0.f ? (m + __log2f(lxt)) * kLn2 : kNegInf;
       }
     }

@@ -18,6 +18,10 @@
 
 #include "fa_kernels.hpp"
 
+#ifndef FA_DECODE_HEADS_PER_ITEM
+#define FA_DECODE_HEADS_PER_ITEM 1   // 0: one kv head per decode work head
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -378,6 +382,21 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
   while (kv_split <= G && (G % kv_split != 0 || (int64_t)(G / kv_split) * Sq > 16)) ++kv_split;
   if (kv_split > G)
     return fail(FA_ERR_UNSUPPORTED, "Sq = %d query positions per kv head; at most 16 are built", Sq);
+  // the other way round, for head rows of at most 128 bytes (D <= 64) when a kv
+  // head has few query rows: 2, 4 or 8 adjacent kv heads form one work head,
+  // which reads their rows of a token as one run of hpi*D elements (longer
+  // contiguous reads stream faster), as long as the run stays within 256
+  // elements and the rows within 16.  The choice depends on the shapes only,
+  // never on the cache layout, so a paged cache and its dense equivalent give
+  // the same bits.
+  int hpi = 1;
+#if FA_DECODE_HEADS_PER_ITEM
+  if (kv_split == 1 && (D == 32 || D == 64))
+    while (D * hpi * 2 <= 256 && Hkv % (hpi * 2) == 0 && (int64_t)G * Sq * hpi * 2 <= 16) hpi *= 2;
+#endif
+  if ((int64_t)B * Sq * Hq * D * 2 > ((int64_t)1 << 31))
+    return fail(FA_ERR_UNSUPPORTED, "q of %lld bytes; the decode takes at most 2^31",
+                (long long)B * Sq * Hq * D * 2);
   if (S_new < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative number of new tokens");
   if (S_new > 0 && (!k_new || !v_new)) return fail(FA_ERR_INVALID_ARGUMENT, "null k_new / v_new");
   const int64_t knd[3] = {(int64_t)S_new * Hkv * D, (int64_t)Hkv * D, D};
@@ -463,8 +482,14 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
   }
   d.out_partial = op; d.lse_partial = lp;
   d.order = B > 64 ? order : nullptr;   // up to 64 sequences are ranked inside the decode kernel
-  d.B = B; d.Sq = Sq; d.Hq = Hq; d.Hkv = Hkv * kv_split; d.group = G / kv_split;
-  d.kv_heads = Hkv; d.kv_split = kv_split;
+  d.B = B; d.Sq = Sq; d.Hq = Hq; d.Hkv = Hkv * kv_split / hpi; d.group = G / kv_split * hpi;
+  d.kv_heads = Hkv / hpi; d.kv_split = kv_split;
+  d.head_dim = D;
+  d.head_shift = 30;
+  if (hpi > 1) {
+    d.head_shift = 0;
+    while ((1 << d.head_shift) < D) ++d.head_shift;
+  }
   d.num_splits = ns;
   d.scale = scale;
   d.softcap = opts ? opts->softcap : 0.f;
@@ -472,7 +497,7 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
   d.causal = opts ? (opts->causal != 0) : 0;
   d.wl = window_side(opts, true);
   d.wr = window_side(opts, false);
-  hipError_t e = fa::launch_decode((fa::Dtype)dtype, D, d, s);
+  hipError_t e = fa::launch_decode((fa::Dtype)dtype, D * hpi, d, s);
   if (e != hipSuccess) return launch_status(e, "decode launch");
 
   fa::CombineParams c{};

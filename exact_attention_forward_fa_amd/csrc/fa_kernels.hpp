@@ -58,6 +58,10 @@ struct DecodeParams {
   int kv_heads;                // kv heads of the cache
   int kv_split;                // work heads per cache head: a cache head's query heads split into
                                // kv_split groups of at most 16 rows, each reading the same K/V
+  int head_dim;                // head dim of q, the cache and the partials; the kernel's D is
+                               // head_dim * (cache heads per work head): a work head may take
+                               // 2, 4 or 8 adjacent cache heads as one row of D elements
+  int head_shift;              // log2(head_dim) when a work head takes several cache heads, else 30
   int num_splits;
   float scale;
   float softcap;

@@ -152,7 +152,12 @@ int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits);
  *   workspace: device memory of at least fa_kvcache_workspace_size() bytes,
  *     256-byte aligned, any contents; it holds the per-split partials between
  *     the kernels.  Calls sharing a workspace must not overlap in time.
- *   B*num_splits*Hkv*(query-head groups per kv head) <= 2^30.
+ *   B*num_splits*Hkv*(query-head groups per kv head) <= 2^30, and q holds at
+ *   most 2^31 bytes (B*Sq*Hq*D*2); FA_ERR_UNSUPPORTED otherwise.
+ *   Arithmetic: at D = 32 and 64, when a kv head has few query rows, 2, 4 or 8
+ *   adjacent kv heads (at most 256 elements together, at most 16 rows) are
+ *   read as one work item; each query then takes its own head's keys exactly
+ *   (the other heads' elements meet zeros), so cache values must be finite.
  */
 fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
                          const int* cache_seqlens, const int* block_table, int block_table_stride,

@@ -120,6 +120,9 @@ def test_kvcache_workspace_and_rejects(lib):
     assert kv(Hq=8, Hkv=8, Sq=17) == 2        # 17 query positions per kv head > 16 (heads split, positions not)
     assert kv(Hq=32, Hkv=1, Sq=17) == 2
     assert kv(page=0) == 1
+    # q of more than 2^31 bytes: B * Sq * Hq * D * 2 = 2^20 * 16 * 8 * 128 * 2
+    assert lib.fa_fwd_kvcache(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 100, 16, FAKE, 1 << 40, FAKE, FAKE,
+                              1 << 20, 16, 8, 8, 128, ob, None) == 2
     assert lib.fa_fwd_kvcache(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 100, 16, FAKE, 1 << 30, FAKE, FAKE,
                               4, 1, 32, 8, 80, ob, None) == 2   # head dim 80: not built
     assert kv(bts=0) == 1
