@@ -336,6 +336,36 @@ def test_decode_head_dims_32_96_256(D, dt, page, paged):
     check(out.cpu(), lse.cpu(), ro, rl, dt, f"decode D={D} page={page} paged={paged}")
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,Sq,dt,opts", [
+    (32, 8, 8, 2, torch.float16, dict(causal=True)),                      # 8 kv heads per work item, 16 rows
+    (64, 8, 4, 2, torch.bfloat16, dict(causal=True, softcap=5.0)),        # 4 per item
+    (64, 6, 6, 1, torch.float16, dict(window=(300, 0), alibi=True)),      # 2 per item (6 = 2 * 3)
+    (32, 12, 4, 1, torch.bfloat16, dict()),                               # 4 per item, 3 query heads each
+])
+def test_decode_adjacent_heads_per_item(D, Hq, Hkv, Sq, dt, opts):
+    """Small head dims read 2, 4 or 8 adjacent kv heads as one work item; every
+    query must still see exactly its own head's keys, and a paged cache and its
+    dense equivalent give the same bits."""
+    print("case decode heads per item", D, Hq, Hkv, Sq, dt, opts, flush=True)
+    lens = [700, 33, 1500, 260]
+    pc = inputs.paged_cache(4, Sq, Hq, Hkv, D, dt, seed=950 + D + Hq + Sq, page_size=64, lengths=lens,
+                            tail_fill="nan")
+    slopes = inputs.alibi_slopes(Hq) if opts.get("alibi") else None
+    kw = dict(causal=opts.get("causal", False), window_size=opts.get("window", (-1, -1)),
+              softcap=opts.get("softcap", 0.0), alibi_slopes=None if slopes is None else slopes.to(DEV))
+    out, lse = fa.fwd_kvcache(pc.q.to(DEV), pc.k_pool.to(DEV), pc.v_pool.to(DEV), pc.cache_seqlens.to(DEV),
+                              block_table=pc.block_table.to(DEV), num_splits=3, **kw)
+    kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
+    vd = inputs.dense_cache_from_pool(pc.v_pool, pc.block_table, pc.cache_seqlens)
+    out2, lse2 = fa.fwd_kvcache(pc.q.to(DEV), kd.to(DEV), vd.to(DEV), pc.cache_seqlens.to(DEV), num_splits=3, **kw)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, 64,
+                                   causal=opts.get("causal", False), window=opts.get("window", (-1, -1)),
+                                   softcap=opts.get("softcap", 0.0), alibi_slopes=slopes)
+    check(out.cpu(), lse.cpu(), ro, rl, dt, f"decode heads per item D={D} Hq={Hq} Hkv={Hkv} Sq={Sq}")
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 def test_paged_decode_many_sequences():
     # more than 64 sequences: the schedule order comes from its own kernel
     lens = [int(x) for x in np.random.default_rng(80).integers(0, 400, 80)]
