@@ -121,3 +121,32 @@ def test_random_kvcache(seed):
     ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, page or 64,
                                    **oracle_kw(c, slopes))
     check(out.cpu(), lse.cpu(), ro, rl, c["dt"], f"random kvcache {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_kvcache_adjacent_heads(seed):
+    """Seeded sweep over the shapes whose decode reads 2, 4 or 8 adjacent kv
+    heads as one work item (D = 32 and 64, kv head counts 2, 4 and 8, few query
+    rows per kv head), with random options, pages and splits."""
+    r = np.random.default_rng(8100 + seed)
+    c = draw(8200 + seed)
+    Hkv = int(r.choice([2, 4, 8]))
+    G = int(r.choice([1, 2]))
+    D = int(r.choice([32, 64]))
+    B = int(r.integers(1, 5))
+    Sq = int(r.integers(1, 3))
+    page = int(r.choice([16, 64, 256]))
+    lens = [int(x) for x in r.integers(Sq, 900, B)]
+    print("case", seed, B, Sq, Hkv * G, Hkv, D, page, lens, c["dt"], c["o"], flush=True)
+    pc = inputs.paged_cache(B, Sq, Hkv * G, Hkv, D, c["dt"], seed=8300 + seed, page_size=page, lengths=lens,
+                            tail_fill="nan")
+    c = dict(c, Hq=Hkv * G)
+    slopes, kw = kw_of(c)
+    sd = None if slopes is None else slopes.to(DEV)
+    ns = int(r.integers(0, 9))
+    out, lse = fa.fwd_kvcache(pc.q.to(DEV), pc.k_pool.to(DEV), pc.v_pool.to(DEV), pc.cache_seqlens.to(DEV),
+                              block_table=pc.block_table.to(DEV), num_splits=ns, alibi_slopes=sd, **kw)
+    torch.cuda.synchronize()
+    ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, page,
+                                   **oracle_kw(c, slopes))
+    check(out.cpu(), lse.cpu(), ro, rl, c["dt"], f"random kvcache adjacent heads {seed}")
