@@ -43,7 +43,7 @@ class FaError(RuntimeError):
 class _Opts(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int),
                 ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
-                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
+                ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p), ("finite_cache", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -118,16 +118,40 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, device):
+def _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, device, Hq, finite_cache=False):
     if alibi_slopes is not None:
         if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or not alibi_slopes.is_contiguous():
             raise ValueError("alibi_slopes must be a contiguous float32 CUDA tensor")
         if alibi_slopes.device != device:
             raise ValueError("alibi_slopes must be on the same device as q")
+        if alibi_slopes.numel() < Hq:
+            raise ValueError(f"alibi_slopes holds {alibi_slopes.numel()} slopes for {Hq} query heads")
+    if softmax_scale is not None and not float(softmax_scale) > 0.0:
+        raise ValueError("softmax_scale must be positive (None selects 1/sqrt(head_dim))")
     o = _Opts(0.0 if softmax_scale is None else float(softmax_scale), int(bool(causal)),
               int(window_size[0]), int(window_size[1]), float(softcap),
-              None if alibi_slopes is None else alibi_slopes.data_ptr())
+              None if alibi_slopes is None else alibi_slopes.data_ptr(), int(bool(finite_cache)))
     return ctypes.byref(o), o
+
+
+def _check_out(out, shape, dtype, device, name="out"):
+    """A caller-supplied output: its shape, dtype and device must be those the call writes
+    (the C ABI sees only a pointer and strides, so a wrong size would write out of bounds)."""
+    if out is None:
+        return
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype or out.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {device}, got "
+                         f"{out.dtype} {tuple(out.shape)} on {out.device}")
+    if out.stride(-1) != 1:
+        raise ValueError(f"{name}: head_dim must be contiguous")
+
+
+def _check_lse(lse, shape, device):
+    if lse is None:
+        return
+    if tuple(lse.shape) != tuple(shape) or lse.dtype != torch.float32 or lse.device != device \
+            or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(shape)} on {device}")
 
 
 def _need_gpu(*ts):
@@ -160,7 +184,6 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), softcap
     of the dequantised values (1 for a direct conversion).
     """
     _unsupported_kwargs(dropout_p, return_attn_probs)
-    _need_gpu(q, k, v)
     if q.dtype == torch.float8_e4m3fn:
         return _fwd_fp8(q, k, v, softmax_scale, causal, window_size, softcap, alibi_slopes, out, lse,
                         q_descale, k_descale, v_descale)
@@ -174,12 +197,15 @@ def fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), softcap
     Sk, Hkv = k.shape[1], k.shape[2]
     if k.shape[0] != B or k.shape[3] != D:
         raise ValueError("batch / head_dim mismatch")
+    _check_out(out, q.shape, q.dtype, q.device)
+    _check_lse(lse, (B, Hq, Sq), q.device)
+    _need_gpu(q, k, v, out, lse)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     lib = load_library()
-    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device, Hq)
     _check(lib.fa_fwd(_DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                       B, Sq, Sk, Hq, Hkv, D, _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)),
                       _strides(v, (0, 1, 2)), _strides(out, (0, 1, 2)), ob, _stream(q.device)))
@@ -198,14 +224,15 @@ def _fwd_fp8(q, k, v, softmax_scale, causal, window_size, softcap, alibi_slopes,
     Sk, Hkv = k.shape[1], k.shape[2]
     if k.shape[0] != B or k.shape[3] != D:
         raise ValueError("batch / head_dim mismatch")
+    _check_out(out, q.shape, torch.bfloat16, q.device)     # fp8 inputs give a bfloat16 out
+    _check_lse(lse, (B, Hq, Sq), q.device)
+    _need_gpu(q, k, v, out, lse)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
-    if out.dtype != torch.bfloat16:
-        raise ValueError("fp8 inputs give a bfloat16 out")
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     lib = load_library()
-    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device, Hq)
     _check(lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D,
                           _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)), _strides(v, (0, 1, 2)),
                           _strides(out, (0, 1, 2)), float(q_descale), float(k_descale), float(v_descale),
@@ -221,24 +248,32 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, 
     Returns (out [total_q,Hq,D], softmax_lse [Hq,total_q] float32).
     """
     _unsupported_kwargs(dropout_p, return_attn_probs)
-    _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float16 or bfloat16")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
         raise ValueError("expected q [total_q,Hq,D] and k, v [total_k,Hkv,D]")
+    if q.stride(-1) != 1 or k.stride(-1) != 1 or v.stride(-1) != 1:
+        raise ValueError("head_dim must be contiguous")
     total_q, Hq, D = q.shape
     total_k, Hkv = k.shape[0], k.shape[1]
+    if k.shape[2] != D:
+        raise ValueError("head_dim mismatch")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.dim() != 1:
+        raise ValueError("cu_seqlens must be 1-D [B+1]")
     B = cu_seqlens_q.numel() - 1
     if cu_seqlens_k.numel() != B + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    _check_out(out, q.shape, q.dtype, q.device)
+    _check_lse(lse, (Hq, total_q), q.device)
+    _need_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     lib = load_library()
-    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device, Hq)
     _check(lib.fa_fwd_varlen(_DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                              _ptr(cu_seqlens_q.contiguous()), _ptr(cu_seqlens_k.contiguous()), B,
                              int(max_seqlen_q), int(max_seqlen_k), total_q, total_k, Hq, Hkv, D,
@@ -258,7 +293,7 @@ def kvcache_num_splits(B, Hkv, max_seqlen_k, num_splits=0) -> int:
 def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits=0, softmax_scale=None,
                 causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None, workspace=None,
                 out=None, lse=None, k=None, v=None, cache_leftpad=None, cache_batch_idx=None,
-                return_softmax_lse=True):
+                return_softmax_lse=True, finite_cache=False):
     """Decode against a dense [B,Smax,Hkv,D] cache, or a page pool [P,page,Hkv,D] with block_table int32 [B,maxp].
 
     Split-KV over ``num_splits`` chunks (0 = library heuristic) followed by the
@@ -268,12 +303,16 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits
     the caches in place at positions cache_seqlens[b] + t, and the queries
     attend to cache_seqlens[b] + S_new tokens; ``cache_seqlens`` itself is left
     unchanged.
+
+    ``finite_cache=True`` promises that the K and V values of every attended
+    token are finite; the decode
+    at head_dim 32 or 64 may then read several adjacent kv heads as one work item
+    (faster, but a non-finite value in one head would reach its neighbours).
     """
     if (k is None) != (v is None):
         raise ValueError("k and v must be given together")
     if cache_leftpad is not None or cache_batch_idx is not None:
         raise NotImplementedError("cache_leftpad / cache_batch_idx are not supported")
-    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table, k, v)
     if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("q and the caches must share dtype float16 or bfloat16")
     if cache_seqlens.dtype != torch.int32:
@@ -281,38 +320,59 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits
     for t in (q, k_cache, v_cache):
         if not t.is_contiguous():
             raise ValueError("q, k_cache and v_cache must be contiguous")
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,Sq,Hq,D] and k_cache, v_cache of one shape [B,Smax,Hkv,D] or "
+                         "[num_pages,page_size,Hkv,D]")
     B, Sq, Hq, D = q.shape
     Hkv = k_cache.shape[2]
+    if k_cache.shape[3] != D:
+        raise ValueError(f"cache head_dim {k_cache.shape[3]} differs from q's {D}")
+    if cache_seqlens.dim() != 1 or cache_seqlens.numel() != B or not cache_seqlens.is_contiguous():
+        raise ValueError(f"cache_seqlens must be contiguous int32 [B={B}]")
     if block_table is not None:
         if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
             raise ValueError("block_table must be int32 [B, max_pages] with unit last stride")
+        if block_table.shape[0] != B:
+            raise ValueError(f"block_table has {block_table.shape[0]} rows for B={B} sequences")
         page, nblocks, bts = k_cache.shape[1], k_cache.shape[0], block_table.stride(0)
+        if block_table.shape[0] > 1 and bts < block_table.shape[1]:
+            raise ValueError("block_table rows overlap")
         smax_bound = bts * page
     else:
+        if k_cache.shape[0] != B:
+            raise ValueError(f"dense k_cache has batch {k_cache.shape[0]}, q has {B}")
         page, nblocks, bts = 0, k_cache.shape[1], 0
         smax_bound = nblocks
-    lib = load_library()
-    ns = int(lib.fa_kvcache_num_splits(B, Hkv, smax_bound, int(num_splits)))
-    need = int(lib.fa_kvcache_workspace_size(B, Sq, Hq, D, ns))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
-    if k is None:
-        _check(lib.fa_fwd_kvcache(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
-                                  _ptr(block_table), bts, page, nblocks, ns, _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-                                  B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
-    else:
+    if k is not None:
         if k.dtype != q.dtype or v.dtype != q.dtype:
             raise ValueError("k and v must share the dtype of q")
         if k.dim() != 4 or k.shape != v.shape or k.shape[0] != B or k.shape[2] != Hkv or k.shape[3] != D:
             raise ValueError("k and v must be [B, S_new, Hkv, D]")
         if k.stride(-1) != 1 or v.stride(-1) != 1:
             raise ValueError("head_dim of k and v must be contiguous")
+    _check_out(out, q.shape, q.dtype, q.device)
+    if out is not None and not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _check_lse(lse, (B, Hq, Sq), q.device)
+    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table, k, v, out, lse, workspace)
+    lib = load_library()
+    ns = int(lib.fa_kvcache_num_splits(B, Hkv, smax_bound, int(num_splits)))
+    need = int(lib.fa_kvcache_workspace_size(B, Sq, Hq, D, ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device, Hq, finite_cache)
+    if k is None:
+        _check(lib.fa_fwd_kvcache(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                  _ptr(block_table), bts, page, nblocks, ns, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                  B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
+    else:
         _check(lib.fa_fwd_kvcache_append(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                          _ptr(cache_seqlens), _ptr(block_table), bts, page, nblocks, ns,
                                          _ptr(k), _ptr(v), k.shape[1], _strides(k, (0, 1, 2)),
@@ -327,13 +387,19 @@ def combine(out_partial, lse_partial, out_dtype=None, out=None, lse=None):
 
     Returns (out [B,S,H,D] in out_dtype (default float16), lse [B,S,H] float32).
     """
-    _need_gpu(out_partial, lse_partial)
     if out_partial.dtype != torch.float32 or lse_partial.dtype != torch.float32:
         raise ValueError("partials must be float32")
     B, S, H, D, n = out_partial.shape
     if tuple(lse_partial.shape) != (B, S, H, n):
         raise ValueError("lse_partial must be [B,S,H,num_splits]")
-    out_dtype = out_dtype or torch.float16
+    out_dtype = out_dtype or (out.dtype if out is not None else torch.float16)
+    if out_dtype not in _DTYPES:
+        raise ValueError("out_dtype must be float16 or bfloat16")
+    _check_out(out, (B, S, H, D), out_dtype, out_partial.device)
+    if lse is not None and (tuple(lse.shape) != (B, S, H) or lse.dtype != torch.float32
+                            or lse.device != out_partial.device or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, S, H)}")
+    _need_gpu(out_partial, lse_partial, out, lse)
     if out is None:
         out = torch.empty((B, S, H, D), dtype=out_dtype, device=out_partial.device)
     if lse is None:
@@ -382,7 +448,7 @@ def bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(
     need = int(lib.fa_bwd_workspace_size(B, Sq, Hq))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device, Hq)
     _check(lib.fa_bwd(_DTYPES[q.dtype], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                       _ptr(dq), _ptr(dk), _ptr(dv), B, Sq, Sk, Hq, Hkv, D,
                       _strides(q, (0, 1, 2)), _strides(k, (0, 1, 2)), _strides(v, (0, 1, 2)),
@@ -423,7 +489,7 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q
     need = int(lib.fa_bwd_workspace_size(1, total_q, Hq))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device)
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device, Hq)
     _check(lib.fa_bwd_varlen(_DTYPES[q.dtype], _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q.contiguous()),
                              _ptr(cu_seqlens_k.contiguous()), B, int(max_seqlen_q), int(max_seqlen_k),

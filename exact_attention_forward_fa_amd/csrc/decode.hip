@@ -359,7 +359,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   // live row sees [wlo, whi], so chunks inside it need no masking.
   V8 qb[KSTEP];
   f32x4 o[DBK];
-  float m = kNegInf, l = 0.f, lx = 0.f, slope = 0.f, ipf = 0.f;
+  float m = kNegInf, lx = 0.f, slope = 0.f, ipf = 0.f;
   int rlo = 0, rhi = -1, wlo = 0, whi = -1;
 
   auto begin_item = [&](const DecodeChunk& d, const u32x4 (&qs)[KSTEP], float sls) __attribute__((always_inline)) {
@@ -383,7 +383,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     if (p.causal) whi = min(whi, ip0);
     if (p.wr >= 0) whi = min(whi, ip0 + p.wr);
     m = kNegInf;
-    l = 0.f;
     lx = 0.f;
 #pragma unroll
     for (int db = 0; db < DBK; ++db) o[db] = f32x4{};
@@ -440,7 +439,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     if (__any(m_new > m + kTauD)) {
       const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
       m = m_new;
-      l *= alpha;
       lx *= alpha;
 #pragma unroll
       for (int db = 0; db < DBK; ++db) o[db] *= alpha;
@@ -448,9 +446,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     const float m_use = m == kNegInf ? 0.f : m;
     // O^T += V^T P^T per 32 tokens: B operand element 4g' + r of lane (n, q4) is
     // P of token 32h + 16g' + 4q4 + r
+    // P goes in two rounded parts, hi = RN(P) and lo = RN(P - hi), each through
+    // its own product, so O carries P to about 2^-22 relative instead of the
+    // half ulp of the input type that rounding P alone would leave.  The extra
+    // products ride on matrix cores that the memory stream leaves idle.
 #pragma unroll
     for (int hh = 0; hh < NG / 2; ++hh) {
-      V8 bop;
+      V8 bop, blo;
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -460,7 +462,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
           const V2 pp = E::pack(p0, p1);
           bop[4 * g + r] = pp[0];
           bop[4 * g + r + 1] = pp[1];
-          l = E::sum2(pp, l);
+          const V2 pl = E::pack(p0 - E::to_f32(pp[0]), p1 - E::to_f32(pp[1]));
+          blo[4 * g + r] = pl[0];
+          blo[4 * g + r + 1] = pl[1];
           lx += p0 + p1;
         }
       // V^T operand rows: 32h + 16g' + 4q4 + (n / 4), columns 16db + 4(n % 4)
@@ -471,15 +475,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
         const i16x4 x1 = lds_read_tr16(vrow + 16 * VROW + db * 16);
         const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
         o[db] = E::mfma16(a, bop, o[db]);
+        o[db] = E::mfma16(a, blo, o[db]);
       }
     }
     if (d.last) {
       // the four lanes of a row hold partial sums over their own tokens
-      const float lt = sum_halves(sum_xor16(l));
       const float lxt = sum_halves(sum_xor16(lx));
       if (live) {
         const int64_t prow = prow_of(d);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float inv = lxt > 0.f ? 1.f / lxt : 0.f;
         // only the row's own cache head's elements of O are its output
         float* dst = p.out_partial + prow * p.head_dim + 4 * q4;
 #pragma unroll

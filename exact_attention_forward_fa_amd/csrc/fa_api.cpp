@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -17,10 +18,6 @@
 #include <vector>
 
 #include "fa_kernels.hpp"
-
-#ifndef FA_DECODE_HEADS_PER_ITEM
-#define FA_DECODE_HEADS_PER_ITEM 1   // 0: one kv head per decode work head
-#endif
 
 namespace {
 
@@ -51,6 +48,8 @@ fa_status check_opts(const fa_attn_opts* o, int D, float* scale_out) {
       return fail(FA_ERR_INVALID_ARGUMENT, "window (%d, %d): each side must be >= -1", o->window_left, o->window_right);
     if (!std::isfinite(o->softcap) || o->softcap < 0.f)
       return fail(FA_ERR_INVALID_ARGUMENT, "softcap must be finite and >= 0");
+    if (o->softmax_scale < 0.f)
+      return fail(FA_ERR_INVALID_ARGUMENT, "softmax_scale %g is negative (0 selects 1/sqrt(D))", o->softmax_scale);
     scale = o->softmax_scale;
   }
   *scale_out = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
@@ -99,7 +98,13 @@ fa_status launch_status(hipError_t e, const char* what) {
   return ok();
 }
 
-constexpr int64_t kMaxGrid = 0x7fffffffLL;
+// An HSA dispatch counts work-items in 32 bits: workgroups times threads per
+// workgroup must stay below 2^32.
+bool dispatch_fits(int64_t groups, int threads) { return groups >= 0 && groups * threads <= 0xffffffffLL; }
+fa_status grid_too_large(int64_t groups, int threads) {
+  return fail(FA_ERR_UNSUPPORTED, "%lld workgroups of %d threads exceed the 2^32 work-items of one dispatch",
+              (long long)groups, threads);
+}
 
 // compute units of the current device (256 if the query fails)
 int device_cus() {
@@ -216,7 +221,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
     return st;
   const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, Sq, device_cus());
   const int64_t nqt = (Sq + bm - 1) / bm;
-  if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (!dispatch_fits(nqt * Hq * (int64_t)B, 512)) return grid_too_large(nqt * Hq * (int64_t)B, 512);
 
   fa::PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
@@ -264,7 +269,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
     return st;
   const int bm = fa::prefill_block_m_fp8(D);
   const int64_t nqt = (Sq + bm - 1) / bm;
-  if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (!dispatch_fits(nqt * Hq * (int64_t)B, 512)) return grid_too_large(nqt * Hq * (int64_t)B, 512);
 
   fa::PrefillParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
@@ -312,7 +317,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
     return st;
   const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, max_seqlen_q, device_cus());
   const int64_t nqt = (max_seqlen_q + bm - 1) / bm;
-  if (nqt * Hq * (int64_t)B > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (!dispatch_fits(nqt * Hq * (int64_t)B, 512)) return grid_too_large(nqt * Hq * (int64_t)B, 512);
   if (debug_checks() && (st = debug_check_cu(cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, max_seqlen_k, total_q,
                                              total_k, (hipStream_t)stream)))
     return st;
@@ -383,17 +388,18 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
   if (kv_split > G)
     return fail(FA_ERR_UNSUPPORTED, "Sq = %d query positions per kv head; at most 16 are built", Sq);
   // the other way round, for head rows of at most 128 bytes (D <= 64) when a kv
-  // head has few query rows: 2, 4 or 8 adjacent kv heads form one work head,
-  // which reads their rows of a token as one run of hpi*D elements (longer
-  // contiguous reads stream faster), as long as the run stays within 256
-  // elements and the rows within 16.  The choice depends on the shapes only,
-  // never on the cache layout, so a paged cache and its dense equivalent give
-  // the same bits.
+  // head has few query rows and the caller vouches that the cache is finite
+  // (opts->finite_cache): 2, 4 or 8 adjacent kv heads form one work head, which
+  // reads their rows of a token as one run of hpi*D elements (longer contiguous
+  // reads stream faster), as long as the run stays within 256 elements and the
+  // rows within 16.  A query then meets the other heads' elements with zeros, so
+  // a non-finite value there would reach its sum; without the promise every
+  // work head reads its own kv head only.  The choice depends on the shapes and
+  // that flag, never on the cache layout, so a paged cache and its dense
+  // equivalent give the same bits.
   int hpi = 1;
-#if FA_DECODE_HEADS_PER_ITEM
-  if (kv_split == 1 && (D == 32 || D == 64))
+  if (opts && opts->finite_cache && kv_split == 1 && (D == 32 || D == 64))
     while (D * hpi * 2 <= 256 && Hkv % (hpi * 2) == 0 && (int64_t)G * Sq * hpi * 2 <= 16) hpi *= 2;
-#endif
   if ((int64_t)B * Sq * Hq * D * 2 > ((int64_t)1 << 31))
     return fail(FA_ERR_UNSUPPORTED, "q of %lld bytes; the decode takes at most 2^31",
                 (long long)B * Sq * Hq * D * 2);
@@ -416,8 +422,8 @@ static fa_status kvcache_impl(fa_dtype dtype, const void* q, void* k_cache, void
     return fail(FA_ERR_UNSUPPORTED, "k_cache/v_cache must be 16-byte aligned");
   if (S_new > 0 && num_blocks_or_smax == 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "new tokens for an empty cache");
-  if (S_new > 0 && (int64_t)B * S_new * Hkv * (D / 8) > (int64_t)kMaxGrid * 256)
-    return fail(FA_ERR_UNSUPPORTED, "too many new tokens for one launch");
+  if (S_new > 0 && !dispatch_fits(((int64_t)B * S_new * Hkv * (D / 8) + 255) / 256, 256))
+    return grid_too_large(((int64_t)B * S_new * Hkv * (D / 8) + 255) / 256, 256);
   // everything the decode needs is checked before anything is launched
   int ns = 0;
   if (Sq > 0) {
@@ -577,9 +583,9 @@ fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k,
   }
   const int bn = fa::backward_block_n(D), bm = fa::backward_block_m(D);
   const int64_t nkt = (Sk + bn - 1) / bn, nqt = (Sq + bm - 1) / bm;
-  if (nkt * B * (int64_t)Hkv > kMaxGrid || nqt * B * (int64_t)Hq > kMaxGrid ||
-      ((int64_t)B * Sq * Hq * (D / 8) + 255) / 256 > kMaxGrid)
-    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (!dispatch_fits(nkt * B * (int64_t)Hkv, 512) || !dispatch_fits(nqt * B * (int64_t)Hq, 512) ||
+      !dispatch_fits(((int64_t)B * Sq * Hq * (D / 8) + 255) / 256, 256))
+    return grid_too_large(std::max(nkt * B * (int64_t)Hkv, nqt * B * (int64_t)Hq), 512);
 
   fa::BackwardParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out; p.dout = dout; p.lse = lse;
@@ -648,9 +654,9 @@ fa_status fa_bwd_varlen(fa_dtype dtype, const void* dout, const void* q, const v
   }
   const int bn = fa::backward_block_n(D), bm = fa::backward_block_m(D);
   const int64_t nkt = (max_seqlen_k + bn - 1) / bn, nqt = (max_seqlen_q + bm - 1) / bm;
-  if (nkt * B * (int64_t)Hkv > kMaxGrid || nqt * B * (int64_t)Hq > kMaxGrid ||
-      ((int64_t)total_q * Hq * (D / 8) + 255) / 256 > kMaxGrid)
-    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (!dispatch_fits(nkt * B * (int64_t)Hkv, 512) || !dispatch_fits(nqt * B * (int64_t)Hq, 512) ||
+      !dispatch_fits(((int64_t)total_q * Hq * (D / 8) + 255) / 256, 256))
+    return grid_too_large(std::max(nkt * B * (int64_t)Hkv, nqt * B * (int64_t)Hq), 512);
   if (debug_checks() && (st = debug_check_cu(cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, max_seqlen_k, total_q,
                                              total_k, (hipStream_t)stream)))
     return st;
@@ -704,7 +710,7 @@ fa_status fa_combine(const float* out_partial, const float* lse_partial, int B, 
     if (ls[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative lse_partial stride");
   for (int i = 0; i < 3; ++i)
     if (oo[i] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative out stride");
-  if (((int64_t)B * S * H + 3) / 4 > kMaxGrid) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (!dispatch_fits(((int64_t)B * S * H + 3) / 4, 256)) return grid_too_large(((int64_t)B * S * H + 3) / 4, 256);
   fa::CombineParams c{};
   c.out_partial = out_partial; c.lse_partial = lse_partial;
   c.op_sb = os[0]; c.op_ss = os[1]; c.op_sh = os[2]; c.op_sd = os[3]; c.op_sn = os[4];

@@ -33,6 +33,9 @@ namespace fa {
 
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
 constexpr float kTauPow = 256.f;   // 2^kTau
+// |out| from which a wave recomputes its rows with P carried in two parts (see
+// the epilogue of prefill_kernel)
+constexpr float kPreciseOut = 1.f;
 
 // Head dims from which the ping-pong kernel is used.  With D = 64 the softmax
 // phase outweighs the MFMA phase and a single wave per SIMD cannot issue VALU
@@ -426,6 +429,43 @@ void prefill_kernel(PrefillParams p) {
     }
   };
 
+  // One tile of the precise pass (see the epilogue): P against the final m, split
+  // into two rounded parts that both go through P V; lx sums the fp32 P.
+  auto step_precise = [&](bool edge, int j0, const T* Ks, const T* Vs) __attribute__((always_inline)) {
+    f32x16 s[RB][KB];
+    scores(edge, j0, Ks, s);
+    float mu[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mu[rb] = m[rb] == kNegInf ? 0.f : m[rb];
+    const T* vbase = Vs + (hi * 4 + ((lane & 15) >> 2)) * VS + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+#pragma unroll
+    for (int c = 0; c < BN / 16; ++c) {
+      const int kb = c >> 1, c2 = c & 1;
+      V8 bh[RB], bl[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = exp2_fast(fmaf(s[rb][kb][8 * c2 + e], mult, -mu[rb]));
+          const T h = E::from_f32(pv);
+          bh[rb][e] = h;
+          bl[rb][e] = E::from_f32(pv - E::to_f32(h));
+          lx[rb] += pv;
+        }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4 x0 = lds_read_tr16(vbase + c * 16 * VS + db * 32);
+        const i16x4 x1 = lds_read_tr16(vbase + (c * 16 + 8) * VS + db * 32);
+        const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          o[rb][db] = E::mfma32(a, bh[rb], o[rb][db]);
+          o[rb][db] = E::mfma32(a, bl[rb], o[rb][db]);
+        }
+      }
+    }
+  };
+
   // ---- tiles in ascending key order.  Liveness and the need for masks are
   // decided per wave from its own rows, so a wave's arithmetic does not depend
   // on how many rows its workgroup holds.
@@ -452,25 +492,78 @@ void prefill_kernel(PrefillParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: out = O / l, lse = ln(sum exp(scores)) = (m + log2 lx) * ln 2
+  // ---- epilogue: out = O / l, lse = ln(sum exp(scores)) = (m + log2 lx) * ln 2.
+  // norm: the row sum that normalises O (l of the rounded P, or lx after the
+  // precise pass, whose O is the product with P itself)
+  auto write_rows = [&](const float (&norm)[RB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float lt = sum_halves(norm[rb]);
+      const float lxt = sum_halves(lx[rb]);
+      if (row_ok[rb]) {
+        const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
+        T* orow = op + (int64_t)qrow[rb] * p.o_ss;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            V2 a = E::pack(o[rb][db][4 * gq] * inv, o[rb][db][4 * gq + 1] * inv);
+            V2 c = E::pack(o[rb][db][4 * gq + 2] * inv, o[rb][db][4 * gq + 3] * inv);
+            u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+            *(u32x2*)(orow + db * 32 + gq * 8 + hi * 4) = w;
+          }
+        if (hi == 0) lp[qrow[rb]] = lxt > 0.f ? (m[rb] + __log2f(lxt)) * kLn2 : kNegInf;
+      }
+    }
+  };
+
+  // Rounding P to the input type before P V perturbs each weight by up to half
+  // an ulp of that type.  Where |out| >= 2 half an ulp of out itself nearly
+  // fills the error bar, so a wave with an output element of magnitude
+  // kPreciseOut or more walks its tiles again: P is taken against the final
+  // row max m (every P <= 2^kTau), split into hi = RN(P) and lo = RN(P - hi),
+  // and O accumulates V hi + V lo, which carries P to about 2^-22 relative.
+  bool need = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float lt = sum_halves(l[rb]);
-    const float lxt = sum_halves(lx[rb]);
-    if (row_ok[rb]) {
-      const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
-      T* orow = op + (int64_t)qrow[rb] * p.o_ss;
+    float om = 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          V2 a = E::pack(o[rb][db][4 * gq] * inv, o[rb][db][4 * gq + 1] * inv);
-          V2 c = E::pack(o[rb][db][4 * gq + 2] * inv, o[rb][db][4 * gq + 3] * inv);
-          u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
-          *(u32x2*)(orow + db * 32 + gq * 8 + hi * 4) = w;
-        }
-      if (hi == 0) lp[qrow[rb]] = lxt > 0.f ? (m[rb] + __log2f(lxt)) * kLn2 : kNegInf;
+      for (int r = 0; r < 16; ++r) om = fmaxf(om, fabsf(o[rb][db][r]));
+    need |= row_ok[rb] && lt > 0.f && om * (p.out_scale / lt) >= kPreciseOut;
+  }
+  const bool wave_need = __any(need);
+  if (!wave_need) write_rows(l);
+  if (__syncthreads_or(wave_need)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[rb][db] = f32x16{};
+      lx[rb] = 0.f;
     }
+    if (t_lo < t_hi) {
+      gload(t_lo);
+      swrite(0);
+    }
+    __syncthreads();
+    for (int t = t_lo; t < t_hi; ++t) {
+      const int buf = (t - t_lo) & 1;
+      if (t + 1 < t_hi) gload(t + 1);
+      const int j0 = t * BN;
+      bool any_live = false, all_full = true;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bool live = blk_live[rb] && j0 + BN - 1 >= lo_min[rb] && j0 <= hi_max[rb];
+        any_live |= live;
+        all_full &= live && j0 >= lo_max[rb] && j0 + BN - 1 <= hi_min[rb];
+      }
+      if (wave_need && any_live) step_precise(!all_full, j0, ksm[buf], vsm[buf]);
+      if (t + 1 < t_hi) swrite(buf ^ 1);
+      __syncthreads();
+    }
+    if (wave_need) write_rows(lx);
   }
 }
 
@@ -554,6 +647,11 @@ void prefill_pp_kernel(PrefillParams p) {
   if (p.wl >= 0) lo_max = max(0, w1 + shift - p.wl);
   if (p.causal) hi_min = min(hi_min, w0 + shift);
   if (p.wr >= 0) hi_min = min(hi_min, w0 + shift + p.wr);
+  // the wave's key range: [j_lo of its first row, j_hi of its last]
+  int j_lo_min = 0, j_hi_max = sk - 1;
+  if (p.wl >= 0) j_lo_min = max(0, w0 + shift - p.wl);
+  if (p.causal) j_hi_max = min(j_hi_max, w1 + shift);
+  if (p.wr >= 0) j_hi_max = min(j_hi_max, w1 + shift + p.wr);
 
   V8 qr[DC];
 #pragma unroll
@@ -726,21 +824,103 @@ void prefill_pp_kernel(PrefillParams p) {
   }
   if (grp == 0) barrier();                 // matches group 1's initial offset
 
-  const float lt = sum_halves(l);
-  const float lxt = sum_halves(lx);
-  if (row_ok) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    T* orow = op + (int64_t)qrow * p.o_ss;
+  // norm: the row sum that normalises O (l of the rounded P, or lx after the
+  // precise pass)
+  auto write_row = [&](float norm) __attribute__((always_inline)) {
+    const float lt = sum_halves(norm);
+    const float lxt = sum_halves(lx);
+    if (row_ok) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      T* orow = op + (int64_t)qrow * p.o_ss;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          V2 a = E::pack(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv);
+          V2 c = E::pack(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
+          u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
+          *(u32x2*)(orow + db * 32 + gq * 8 + hi * 4) = w;
+        }
+      if (hi == 0) lp[qrow] = lxt > 0.f ? (m + __log2f(lxt)) * kLn2 : kNegInf;
+    }
+  };
+
+  // The precise pass of prefill_kernel, here as a plain loop over one LDS stage:
+  // waves with an output element of magnitude kPreciseOut or more recompute
+  // their row with P split into RN(P) and RN(P - RN(P)) against the final m.
+  bool need = false;
+  {
+    const float lt = sum_halves(l);
+    float om = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        V2 a = E::pack(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv);
-        V2 c = E::pack(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv);
-        u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, c)};
-        *(u32x2*)(orow + db * 32 + gq * 8 + hi * 4) = w;
+      for (int r = 0; r < 16; ++r) om = fmaxf(om, fabsf(o[db][r]));
+    need = row_ok && lt > 0.f && om / lt >= kPreciseOut;
+  }
+  const bool wave_need = __any(need);
+  if (!wave_need) write_row(l);
+  if (__syncthreads_or(wave_need)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    lx = 0.f;
+    const float mu = m == kNegInf ? 0.f : m;
+    const T* kb_ = ksm[0] + l32 * KS + hi * 8;
+    const T* vb_ = vsm[0] + (hi * 4 + ((lane & 15) >> 2)) * VS + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+    for (int i = 0; i < n_t; ++i) {
+      gload(i);
+      barrier();                             // every wave is done with the previous tile
+      swrite(0);
+      barrier();                             // the tile is in LDS
+      if (!wave_need) continue;
+      const int j0 = (t_lo + i) * BN;
+      if (j0 + BN - 1 < j_lo_min || j0 > j_hi_max) continue;   // no row of the wave sees the tile
+      f32x16 sp[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sp[kb] = f32x16{};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sp[kb] = E::mfma32(*(const V8*)(kb_ + kb * 32 * KS + dc * 16), qr[dc], sp[kb]);
+      const float dj0 = (float)(j0 + 4 * hi) - ipf;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sp[kb][r];
+          if constexpr (SOFTCAP) {
+            const float e = exp2_fast(x * cap_in);
+            x = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
+          } else if constexpr (ALIBI) {
+            x *= sl2;
+          }
+          if constexpr (ALIBI) x = fmaf(-slope_l2, fabsf(dj0 + (float)(kb * 32 + (r >> 2) * 8 + (r & 3))), x);
+          const int jj = j0 + 4 * hi + kb * 32 + (r >> 2) * 8 + (r & 3);
+          sp[kb][r] = (jj < j_lo || jj > j_hi) ? kNegInf : x;
+        }
+#pragma unroll
+      for (int c = 0; c < BN / 16; ++c) {
+        const int kb = c >> 1, c2 = c & 1;
+        V8 bh, bl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = exp2_fast(fmaf(sp[kb][8 * c2 + e], mult, -mu));
+          const T h = E::from_f32(pv);
+          bh[e] = h;
+          bl[e] = E::from_f32(pv - E::to_f32(h));
+          lx += pv;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const i16x4 x0 = lds_read_tr16(vb_ + c * 16 * VS + db * 32);
+          const i16x4 x1 = lds_read_tr16(vb_ + (c * 16 + 8) * VS + db * 32);
+          const V8 a = __builtin_bit_cast(V8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = E::mfma32(a, bh, o[db]);
+          o[db] = E::mfma32(a, bl, o[db]);
+        }
       }
-    if (hi == 0) lp[qrow] = lxt > 0.f ? (m + __log2f(lxt)) * kLn2 : kNegInf;
+    }
+    if (wave_need) write_row(lx);
   }
 }
 

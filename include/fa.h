@@ -60,12 +60,16 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
 /* Attention options ("FlashAttention 常用接口简单介绍", §3.1 keyword arguments). */
 typedef struct {
-  float softmax_scale;          /* <= 0 selects the default 1/sqrt(D)                           */
+  float softmax_scale;          /* 0 selects the default 1/sqrt(D); negative is invalid          */
   int causal;                   /* nonzero: key j allowed for query i iff j <= i + Sk - Sq       */
   int window_left;              /* local window: keys in [i' - left, i' + right], i' = i + Sk - Sq; */
   int window_right;             /*   -1 = unbounded on that side; both -1 = global attention    */
   float softcap;                /* > 0: score s becomes softcap * tanh(s / softcap); 0 = off    */
   const float* alibi_slopes;    /* device float32 [Hq]: score -= slope[h] * |i' - j|; NULL = off */
+  int finite_cache;             /* KV-cache calls only: nonzero promises that the K and V values   */
+                                /*   of every attended token are finite, which lets the decode at */
+                                /*   D = 32 or 64 read 2-8 adjacent kv heads as one work item;    */
+                                /*   0 = each kv head is read alone                               */
 } fa_attn_opts;
 
 /*
@@ -154,10 +158,15 @@ int fa_kvcache_num_splits(int B, int Hkv, int max_seqlen_k, int num_splits);
  *     the kernels.  Calls sharing a workspace must not overlap in time.
  *   B*num_splits*Hkv*(query-head groups per kv head) <= 2^30, and q holds at
  *   most 2^31 bytes (B*Sq*Hq*D*2); FA_ERR_UNSUPPORTED otherwise.
- *   Arithmetic: at D = 32 and 64, when a kv head has few query rows, 2, 4 or 8
- *   adjacent kv heads (at most 256 elements together, at most 16 rows) are
- *   read as one work item; each query then takes its own head's keys exactly
- *   (the other heads' elements meet zeros), so cache values must be finite.
+ *   Arithmetic: each query head's scores take its own kv head's keys only.
+ *   With opts->finite_cache set, at D = 32 and 64 and few query rows per kv
+ *   head, 2, 4 or 8 adjacent kv heads (at most 256 elements together, at most
+ *   16 rows) are read as one work item and each query meets the other heads'
+ *   elements with zeros: exact for finite caches, while one Inf or NaN in a
+ *   neighbouring head would then reach every head of the item.
+ *   num_splits = 0 resolves with max_seqlen_k = the cache capacity
+ *   (block_table_stride * page_size, or Smax); a paged cache and a dense cache
+ *   of equal capacity take the same split count and give the same bits.
  */
 fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
                          const int* cache_seqlens, const int* block_table, int block_table_stride,

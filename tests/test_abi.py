@@ -244,3 +244,84 @@ def test_python_layer_rejects_unsupported_kwargs():
         fa.fwd_kvcache(q, q, q, torch.zeros(1, dtype=torch.int32), k=q)
     with pytest.raises(ValueError):          # CPU tensors: no fallback path exists
         fa.fwd(q, q, q)
+
+
+def test_negative_scale_rejected(lib):
+    """softmax_scale 0 selects 1/sqrt(D); a negative scale is an error, not a silent default."""
+    assert fwd(lib, scale=-0.5) == 1
+    assert "negative" in lib.fa_last_error().decode()
+    assert fwd(lib, scale=-0.5, ptrs=[None] * 5, B=0) == 1      # checked even when there is no work
+
+
+def test_dispatch_work_item_bound(lib):
+    """One dispatch holds at most 2^32 - 1 work-items (workgroups x threads); larger
+    grids are FA_ERR_UNSUPPORTED before anything is launched, for every kernel."""
+    # prefill: 33 query tiles x 64 heads x 4096 batches = 8.65M workgroups of 512 threads > 2^32
+    assert fwd(lib, B=4096, Sq=33 * 256, Sk=8, Hq=64, Hkv=64) == 2
+    assert "2^32" in lib.fa_last_error().decode()
+    assert fwd(lib, B=4096, Sq=31 * 256, Sk=8, Hq=64, Hkv=64) != 2 or "2^32" not in lib.fa_last_error().decode()
+    ob, keep = _opts()
+    # KV append: B * S_new * Hkv * D/8 = 2^16 * 2^10 * 8 * 16 = 2^33 copy lanes
+    assert lib.fa_fwd_kvcache_append(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 100, 16, FAKE, FAKE, 1 << 10,
+                                     None, None, FAKE, 1 << 30, FAKE, FAKE, 1 << 16, 1, 8, 8, 128, ob, None) == 2
+    assert "2^32" in lib.fa_last_error().decode()
+    # combine: B * S * H = 2^27 rows, 4 per 256-thread workgroup = 2^33 work-items
+    assert lib.fa_combine(FAKE, FAKE, 1 << 14, 1 << 7, 1 << 6, 64, 4, None, None, 0, FAKE, None, None, None) == 2
+    assert "2^32" in lib.fa_last_error().decode()
+    # backward: 8.65M dQ workgroups
+    WS = ctypes.c_void_p(1 << 21)
+    assert lib.fa_bwd(0, *([FAKE] * 9), 4096, 33 * 256, 8, 64, 64, 64, None, None, None, None, None, ob, WS,
+                      1 << 40, None) == 2
+    assert "2^32" in lib.fa_last_error().decode()
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.float16)
+
+
+def test_python_layer_checks_shapes_before_anything_runs():
+    """The binding validates what the C ABI cannot see (tensor sizes) before any
+    launch: mismatched caches, tables, lengths, outputs and slopes raise ValueError
+    (checked here on CPU tensors, where the shape check comes first)."""
+    import torch
+    i32 = torch.int32
+    q = _cpu(2, 1, 8, 64)
+    kc = _cpu(10, 16, 2, 64)                       # page pool [P, page, Hkv, D]
+    lens = torch.ones(2, dtype=i32)
+    bt = torch.zeros(2, 4, dtype=i32)
+    cases = [
+        (dict(cache_seqlens=torch.ones(3, dtype=i32)), "cache_seqlens"),
+        (dict(block_table=torch.zeros(3, 4, dtype=i32)), "block_table"),
+        (dict(v_cache=_cpu(10, 16, 2, 32)), "one shape"),
+        (dict(k_cache=_cpu(10, 16, 2, 32), v_cache=_cpu(10, 16, 2, 32)), "head_dim"),
+        (dict(block_table=None, k_cache=_cpu(3, 16, 2, 64), v_cache=_cpu(3, 16, 2, 64)), "batch"),
+        (dict(out=_cpu(2, 1, 8, 32)), "out must be"),
+        (dict(out=_cpu(2, 1, 8, 64, dtype=torch.bfloat16)), "out must be"),
+        (dict(lse=torch.zeros(2, 8, 2)), "lse must be"),
+        (dict(k=_cpu(2, 1, 3, 64), v=_cpu(2, 1, 3, 64)), "S_new"),
+    ]
+    for over, match in cases:
+        args = dict(q=q, k_cache=kc, v_cache=kc, cache_seqlens=lens, block_table=bt)
+        args.update(over)
+        with pytest.raises(ValueError, match=match):
+            fa.fwd_kvcache(**args)
+    qd, kd = _cpu(1, 8, 4, 64), _cpu(1, 8, 2, 64)
+    with pytest.raises(ValueError, match="out must be"):
+        fa.fwd(qd, kd, kd, out=_cpu(1, 8, 4, 32))
+    with pytest.raises(ValueError, match="lse must be"):
+        fa.fwd(qd, kd, kd, lse=torch.zeros(1, 4, 7))
+    with pytest.raises(ValueError, match="lse must be"):
+        fa.fwd(qd, kd, kd, lse=torch.zeros(1, 4, 8, dtype=torch.float64))
+    with pytest.raises(ValueError, match="batch / head_dim"):
+        fa.fwd(qd, _cpu(2, 8, 2, 64), _cpu(2, 8, 2, 64))
+    cu = torch.tensor([0, 8], dtype=i32)
+    with pytest.raises(ValueError, match="lse must be"):
+        fa.fwd_varlen(qd[0], kd[0], kd[0], cu, cu, 8, 8, lse=torch.zeros(4, 9))
+    with pytest.raises(ValueError, match="head_dim"):
+        fa.fwd_varlen(qd[0], kd[0, :, :, :32], kd[0, :, :, :32], cu, cu, 8, 8)
+    op, lp = torch.zeros(1, 1, 2, 64, 3), torch.zeros(1, 1, 2, 3)
+    with pytest.raises(ValueError, match="out must be"):
+        fa.combine(op, lp, out=_cpu(1, 1, 2, 32))
+    with pytest.raises(ValueError, match="lse must be"):
+        fa.combine(op, lp, lse=torch.zeros(1, 1, 3))

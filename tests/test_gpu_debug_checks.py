@@ -64,7 +64,7 @@ def test_cu_seqlens_beyond_total_rejected_forward_and_backward(debug):
     q, k, v, cq, ck = _varlen([100, 60, 40])                             # 200 rows allocated
     out, lse = fa.fwd_varlen(q, k, v, cq, ck, 100, 100, causal=True)
     lib = fa.load_library()
-    ob, keep = fa._opts(None, True, (-1, -1), 0.0, None, q.device)
+    ob, keep = fa._opts(None, True, (-1, -1), 0.0, None, q.device, q.shape[1])
     lse_big = torch.empty((2, 200), dtype=torch.float32, device=DEV)
     # declare 150 rows while cu_seqlens end at 200
     st = lib.fa_fwd_varlen(0, fa._ptr(q), fa._ptr(k), fa._ptr(v), fa._ptr(out), fa._ptr(lse_big), fa._ptr(cq),

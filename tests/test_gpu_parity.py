@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Small workloads are compared element by element in full; the full-size
-workloads on sampled query rows (every batch and head), which the oracle
-evaluates one by one.  Paged vs dense-cache decode and varlen vs per-sequence
+Every workload is compared element by element in full: the full-size ones
+(configs 3 and 4, the fp8 leg) with the oracle run over all (batch, head)
+pairs in parallel worker processes (tests/oracle_pool.py).  Paged vs dense-cache decode and varlen vs per-sequence
 dense are compared bit for bit on the GPU.
 """
 
@@ -14,6 +14,7 @@ import exact_attention_forward_fa_amd as fa
 from exact_attention_forward_fa_amd import inputs
 from oracle import ref
 
+import oracle_pool
 from parity import check
 
 pytestmark = pytest.mark.gpu
@@ -75,25 +76,19 @@ def test_c2_varlen_full_and_bitexact_vs_dense():
         assert torch.equal(ld[0], lse[:, a:e]), f"seq {b} lse differs from dense"
 
 
-# ---------------------------------------------------------------- full-size workloads, sampled rows
-
-def _sample_rows(S, extra_seed):
-    base = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 511, S // 2 - 1, S // 2, S - 129, S - 128,
-            S - 65, S - 2, S - 1]
-    rng = np.random.default_rng(extra_seed)
-    rows = sorted(set([r for r in base if 0 <= r < S] + rng.integers(0, S, 8).tolist()))
-    return rows
-
+# ---------------------------------------------------------------- full-size workloads, every row
 
 @pytest.mark.parametrize("name", ["c3_causal", "c3_win256_0", "c3_win256_256", "c4_gqa"])
-def test_full_size_sampled_rows(name):
+def test_full_size_all_rows(name):
+    """Configs 3 and 4 at full size, in the launch configuration the benchmark
+    times, against the oracle on every row of every (batch, head)."""
     print("case", name, flush=True)
     c = inputs.case(name)
     out, lse = run_dense(c)
-    S = c["q"].shape[1]
-    rows = _sample_rows(S, 5)
-    ro, rl = oracle_dense(c, rows=rows)
-    check(out[:, rows], lse[:, :, rows], ro, rl, c["q"].dtype, name)
+    ro, rl = oracle_pool.dense_full(c["q"], c["k"], c["v"], softmax_scale=c.get("softmax_scale"),
+                                    causal=c.get("causal", False), window=c.get("window", (-1, -1)),
+                                    softcap=c.get("softcap", 0.0), alibi_slopes=c.get("alibi_slopes"))
+    check(out, lse, ro, rl, c["q"].dtype, name)
     # determinism: a second run is bit-identical
     out2, lse2 = run_dense(c)
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
@@ -343,16 +338,17 @@ def test_decode_head_dims_32_96_256(D, dt, page, paged):
     (32, 12, 4, 1, torch.bfloat16, dict()),                               # 4 per item, 3 query heads each
 ])
 def test_decode_adjacent_heads_per_item(D, Hq, Hkv, Sq, dt, opts):
-    """Small head dims read 2, 4 or 8 adjacent kv heads as one work item; every
-    query must still see exactly its own head's keys, and a paged cache and its
-    dense equivalent give the same bits."""
+    """With finite_cache=True, small head dims read 2, 4 or 8 adjacent kv heads
+    as one work item; every query must still see exactly its own head's keys,
+    and a paged cache and its dense equivalent give the same bits."""
     print("case decode heads per item", D, Hq, Hkv, Sq, dt, opts, flush=True)
     lens = [700, 33, 1500, 260]
     pc = inputs.paged_cache(4, Sq, Hq, Hkv, D, dt, seed=950 + D + Hq + Sq, page_size=64, lengths=lens,
                             tail_fill="nan")
     slopes = inputs.alibi_slopes(Hq) if opts.get("alibi") else None
     kw = dict(causal=opts.get("causal", False), window_size=opts.get("window", (-1, -1)),
-              softcap=opts.get("softcap", 0.0), alibi_slopes=None if slopes is None else slopes.to(DEV))
+              softcap=opts.get("softcap", 0.0), alibi_slopes=None if slopes is None else slopes.to(DEV),
+              finite_cache=True)
     out, lse = fa.fwd_kvcache(pc.q.to(DEV), pc.k_pool.to(DEV), pc.v_pool.to(DEV), pc.cache_seqlens.to(DEV),
                               block_table=pc.block_table.to(DEV), num_splits=3, **kw)
     kd = inputs.dense_cache_from_pool(pc.k_pool, pc.block_table, pc.cache_seqlens)
@@ -364,6 +360,43 @@ def test_decode_adjacent_heads_per_item(D, Hq, Hkv, Sq, dt, opts):
                                    softcap=opts.get("softcap", 0.0), alibi_slopes=slopes)
     check(out.cpu(), lse.cpu(), ro, rl, dt, f"decode heads per item D={D} Hq={Hq} Hkv={Hkv} Sq={Sq}")
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("D,dt", [(32, torch.float16), (64, torch.bfloat16)])
+def test_decode_nonfinite_value_stays_in_its_head(D, dt):
+    """Without finite_cache every query head reads its own kv head only: an Inf
+    in kv head 1's K and a NaN in its V leave every other head's out and lse
+    bit-identical to the decode of the finite cache (8 kv heads of one query
+    row each, the shape that finite_cache would read 4-8 heads at a time)."""
+    print("case nonfinite head", D, dt, flush=True)
+    pc = inputs.paged_cache(3, 1, 8, 8, D, dt, seed=960 + D, page_size=64, lengths=[300, 130, 77])
+    kp, vp = pc.k_pool.clone(), pc.v_pool.clone()
+    for b, t in ((0, 5), (1, 129), (2, 40)):
+        page = int(pc.block_table[b, t // 64])
+        kp[page, t % 64, 1, 3] = float("inf")
+        vp[page, (t + 1) % 64, 1, 0] = float("nan")
+    args = dict(block_table=pc.block_table.to(DEV), num_splits=2, causal=True)
+    a = fa.fwd_kvcache(pc.q.to(DEV), pc.k_pool.to(DEV), pc.v_pool.to(DEV), pc.cache_seqlens.to(DEV), **args)
+    b = fa.fwd_kvcache(pc.q.to(DEV), kp.to(DEV), vp.to(DEV), pc.cache_seqlens.to(DEV), **args)
+    torch.cuda.synchronize()
+    others = [h for h in range(8) if h != 1]
+    assert torch.equal(a[0][:, :, others], b[0][:, :, others])
+    assert torch.equal(a[1][:, others], b[1][:, others])
+    assert not torch.isfinite(b[0][:, :, 1]).all()        # the planted head itself is affected
+    ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, 64, causal=True)
+    check(a[0].cpu(), a[1].cpu(), ro, rl, dt, f"nonfinite head D={D} (finite cache)")
+
+
+def test_c5_default_splits_paged_equals_dense_bitexact(c5):
+    """num_splits = 0 resolves from the cache capacity; a dense cache of the
+    paged cache's capacity (block-table width x page size) takes the same split
+    count and gives the same bits."""
+    cap = c5["block_table"].shape[1] * c5["page_size"]
+    kd = inputs.dense_cache_from_pool(c5["k_pool"], c5["block_table"], c5["cache_seqlens"], smax=cap)
+    vd = inputs.dense_cache_from_pool(c5["v_pool"], c5["block_table"], c5["cache_seqlens"], smax=cap)
+    a = run_paged(c5, num_splits=0)
+    b = run_paged(c5, block_table=False, dense=(kd, vd), num_splits=0)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 def test_paged_decode_many_sequences():
@@ -630,19 +663,18 @@ def test_fp8_prefill(case):
     check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"fp8 {case}")
 
 
-def test_fp8_prefill_full_size_sampled_rows():
+def test_fp8_prefill_full_size_all_rows():
     """The fp8 prefill at the size and in the launch configuration the benchmark
     times (B=4, S=4096, H=32, D=64 causal, the fp16 inputs converted to e4m3,
-    descales 1), checked on sampled rows against the oracle on the e4m3 values."""
+    descales 1), checked on every row against the oracle on the e4m3 values."""
     print("case fp8 c3_causal", flush=True)
     c = inputs.case("c3_causal")
     q8, k8, v8 = (c[x].to(torch.float8_e4m3fn) for x in ("q", "k", "v"))
     out, lse = fa.fwd(q8.to(DEV), k8.to(DEV), v8.to(DEV), causal=True)
     torch.cuda.synchronize()
     assert out.dtype == torch.bfloat16
-    rows = _sample_rows(q8.shape[1], 9)
-    ro, rl = ref.attention(q8.double(), k8.double(), v8.double(), causal=True, rows=rows)
-    check(out.cpu()[:, rows], lse.cpu()[:, :, rows], ro, rl, torch.bfloat16, "fp8 c3_causal")
+    ro, rl = oracle_pool.dense_full(q8, k8, v8, causal=True)
+    check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, "fp8 c3_causal")
 
 
 @pytest.mark.parametrize("opts", [dict(causal=True), dict(window=(100, 20)), dict(causal=True, softcap=8.0)])

@@ -125,8 +125,8 @@ def test_random_kvcache(seed):
 
 @pytest.mark.parametrize("seed", range(16))
 def test_random_kvcache_adjacent_heads(seed):
-    """Seeded sweep over the shapes whose decode reads 2, 4 or 8 adjacent kv
-    heads as one work item (D = 32 and 64, kv head counts 2, 4 and 8, few query
+    """Seeded sweep over the shapes whose decode, with finite_cache=True, reads
+    2, 4 or 8 adjacent kv heads as one work item (D = 32 and 64, kv head counts 2, 4 and 8, few query
     rows per kv head), with random options, pages and splits."""
     r = np.random.default_rng(8100 + seed)
     c = draw(8200 + seed)
@@ -145,7 +145,8 @@ def test_random_kvcache_adjacent_heads(seed):
     sd = None if slopes is None else slopes.to(DEV)
     ns = int(r.integers(0, 9))
     out, lse = fa.fwd_kvcache(pc.q.to(DEV), pc.k_pool.to(DEV), pc.v_pool.to(DEV), pc.cache_seqlens.to(DEV),
-                              block_table=pc.block_table.to(DEV), num_splits=ns, alibi_slopes=sd, **kw)
+                              block_table=pc.block_table.to(DEV), num_splits=ns, alibi_slopes=sd,
+                              finite_cache=True, **kw)
     torch.cuda.synchronize()
     ro, rl = ref.attention_kvcache(pc.q, pc.k_pool, pc.v_pool, pc.cache_seqlens, pc.block_table, page,
                                    **oracle_kw(c, slopes))

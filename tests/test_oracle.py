@@ -537,3 +537,21 @@ def test_fp8_e4m3_decoding_matches_the_format_definition():
         mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
         assert got[c] == (-mag if s else mag), (c, got[c], mag)
     assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def test_oracle_pool_equals_oracle():
+    """The parallel driver of the full-size parity tests returns what the oracle
+    returns when called on the whole tensors, up to the rounding order of the
+    library matmul on a row block (1e-12), including GQA, softcap, ALiBi and a
+    window, over more rows than one block."""
+    import oracle_pool
+    from exact_attention_forward_fa_amd import inputs
+    q, k, v = inputs.dense_qkv(2, 1100, 1030, 4, 2, 16, torch.float16, seed=77)
+    slopes = inputs.alibi_slopes(4)
+    kw = dict(causal=True, window=(300, 0), softcap=5.0, alibi_slopes=slopes, softmax_scale=0.3)
+    po, pl = oracle_pool.dense_full(q, k, v, **kw)
+    ro, rl = ref.attention(q, k, v, **kw)
+    assert np.abs(po - ro).max() <= 1e-12
+    assert (np.isneginf(pl) == np.isneginf(rl)).all()
+    fin = np.isfinite(rl)
+    assert np.abs(pl[fin] - rl[fin]).max() <= 1e-12
