@@ -25,8 +25,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "combine", "bwd", "bwd_varlen", "attention", "attention_varlen", "kvcache_workspace_size",
-           "kvcache_num_splits", "bwd_workspace_size", "library_path", "load_library", "FaError"]
+__all__ = ["fwd", "fwd_varlen", "fwd_kvcache", "fwd_kvcache_noalloc", "combine", "bwd", "bwd_varlen", "attention", "attention_varlen", "kvcache_workspace_size",
+           "kvcache_num_splits", "kvcache_noalloc_max_bytes", "bwd_workspace_size", "library_path", "load_library", "FaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa.so")
@@ -76,6 +76,10 @@ def load_library():
     lib.fa_fwd_kvcache_append.argtypes = [I, P, P, P, P, P, I, I, I, I, P, P, I, I64P, I64P, P, Z, P, P,
                                           I, I, I, I, I, OP, P]
     lib.fa_fwd_kvcache_append.restype = I
+    lib.fa_kvcache_noalloc_max_bytes.argtypes = []
+    lib.fa_kvcache_noalloc_max_bytes.restype = Z
+    lib.fa_fwd_kvcache_noalloc.argtypes = [I, P, P, P, P, P, I, I, I, I, P, P, I, I, I, I, I, OP, P]
+    lib.fa_fwd_kvcache_noalloc.restype = I
     lib.fa_combine.argtypes = [P, P, I, I, I, I, I, I64P, I64P, I, P, I64P, P, P]
     lib.fa_combine.restype = I
     lib.fa_bwd_workspace_size.argtypes = [I, I, I]
@@ -290,31 +294,9 @@ def kvcache_num_splits(B, Hkv, max_seqlen_k, num_splits=0) -> int:
     return int(load_library().fa_kvcache_num_splits(B, Hkv, max_seqlen_k, num_splits))
 
 
-def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits=0, softmax_scale=None,
-                causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None, workspace=None,
-                out=None, lse=None, k=None, v=None, cache_leftpad=None, cache_batch_idx=None,
-                return_softmax_lse=True, finite_cache=False):
-    """Decode against a dense [B,Smax,Hkv,D] cache, or a page pool [P,page,Hkv,D] with block_table int32 [B,maxp].
-
-    Split-KV over ``num_splits`` chunks (0 = library heuristic) followed by the
-    LSE combine.  Returns (out [B,Sq,Hq,D], softmax_lse [B,Hq,Sq]).
-
-    With ``k`` and ``v`` ([B,S_new,Hkv,D]) the new tokens are first written into
-    the caches in place at positions cache_seqlens[b] + t, and the queries
-    attend to cache_seqlens[b] + S_new tokens; ``cache_seqlens`` itself is left
-    unchanged.
-
-    ``finite_cache=True`` promises that the K and V values of every attended
-    token are finite; the decode
-    at head_dim 32 or 64 may then read several adjacent kv heads as one work item
-    (faster, but a non-finite value in one head would reach its neighbours).
-    """
-    if (k is None) != (v is None):
-        raise ValueError("k and v must be given together")
-    if cache_leftpad is not None or cache_batch_idx is not None:
-        raise NotImplementedError("cache_leftpad / cache_batch_idx are not supported")
-    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("q and the caches must share dtype float16 or bfloat16")
+def _kvcache_shapes(q, k_cache, v_cache, cache_seqlens, block_table):
+    """Shapes of a KV-cache call, checked; returns (B, Sq, Hq, D, Hkv, page, nblocks,
+    block-table stride, cache capacity)."""
     if cache_seqlens.dtype != torch.int32:
         raise ValueError("cache_seqlens must be int32")
     for t in (q, k_cache, v_cache):
@@ -343,6 +325,36 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits
             raise ValueError(f"dense k_cache has batch {k_cache.shape[0]}, q has {B}")
         page, nblocks, bts = 0, k_cache.shape[1], 0
         smax_bound = nblocks
+    return B, Sq, Hq, D, Hkv, page, nblocks, bts, smax_bound
+
+
+def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits=0, softmax_scale=None,
+                causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None, workspace=None,
+                out=None, lse=None, k=None, v=None, cache_leftpad=None, cache_batch_idx=None,
+                return_softmax_lse=True, finite_cache=False):
+    """Decode against a dense [B,Smax,Hkv,D] cache, or a page pool [P,page,Hkv,D] with block_table int32 [B,maxp].
+
+    Split-KV over ``num_splits`` chunks (0 = library heuristic) followed by the
+    LSE combine.  Returns (out [B,Sq,Hq,D], softmax_lse [B,Hq,Sq]).
+
+    With ``k`` and ``v`` ([B,S_new,Hkv,D]) the new tokens are first written into
+    the caches in place at positions cache_seqlens[b] + t, and the queries
+    attend to cache_seqlens[b] + S_new tokens; ``cache_seqlens`` itself is left
+    unchanged.
+
+    ``finite_cache=True`` promises that the K and V values of every attended
+    token are finite; the decode
+    at head_dim 32 or 64 may then read several adjacent kv heads as one work item
+    (faster, but a non-finite value in one head would reach its neighbours).
+    """
+    if (k is None) != (v is None):
+        raise ValueError("k and v must be given together")
+    if cache_leftpad is not None or cache_batch_idx is not None:
+        raise NotImplementedError("cache_leftpad / cache_batch_idx are not supported")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share dtype float16 or bfloat16")
+    B, Sq, Hq, D, Hkv, page, nblocks, bts, smax_bound = _kvcache_shapes(q, k_cache, v_cache, cache_seqlens,
+                                                                         block_table)
     if k is not None:
         if k.dtype != q.dtype or v.dtype != q.dtype:
             raise ValueError("k and v must share the dtype of q")
@@ -380,6 +392,36 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, num_splits
                                          workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                          B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
     return (out, lse) if return_softmax_lse else out
+
+
+def fwd_kvcache_noalloc(q, k_cache, v_cache, cache_seqlens, out, lse, block_table=None, num_splits=0,
+                        softmax_scale=None, causal=False, window_size=(-1, -1), softcap=0.0, alibi_slopes=None,
+                        finite_cache=False):
+    """``fwd_kvcache`` (without new keys) through the entry point that allocates
+    nothing: the decode workspace is the library's static device array, and the
+    caller passes ``out`` [B,Sq,Hq,D] and ``lse`` [B,Hq,Sq].  Calls that overlap
+    in time on one GPU share that array and race.  Returns (out, lse)."""
+    if out is None or lse is None:
+        raise ValueError("fwd_kvcache_noalloc writes into caller-given out and lse")
+    if q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share dtype float16 or bfloat16")
+    B, Sq, Hq, D, Hkv, page, nblocks, bts, _ = _kvcache_shapes(q, k_cache, v_cache, cache_seqlens, block_table)
+    _check_out(out, q.shape, q.dtype, q.device)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    _check_lse(lse, (B, Hq, Sq), q.device)
+    _need_gpu(q, k_cache, v_cache, cache_seqlens, block_table, out, lse)
+    lib = load_library()
+    ob, keep = _opts(softmax_scale, causal, window_size, softcap, alibi_slopes, q.device, Hq, finite_cache)
+    _check(lib.fa_fwd_kvcache_noalloc(_DTYPES[q.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                      _ptr(block_table), bts, page, nblocks, int(num_splits), _ptr(out), _ptr(lse),
+                                      B, Sq, Hq, Hkv, D, ob, _stream(q.device)))
+    return out, lse
+
+
+def kvcache_noalloc_max_bytes() -> int:
+    """Size of the static decode workspace behind ``fwd_kvcache_noalloc``."""
+    return int(load_library().fa_kvcache_noalloc_max_bytes())
 
 
 def combine(out_partial, lse_partial, out_dtype=None, out=None, lse=None):

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -528,6 +530,64 @@ fa_status fa_fwd_kvcache(fa_dtype dtype, const void* q, const void* k_cache, con
   return kvcache_impl(dtype, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), cache_seqlens, block_table,
                       block_table_stride, page_size, num_blocks_or_smax, num_splits, workspace, workspace_bytes,
                       out, lse, B, Sq, Hq, Hkv, D, opts, stream, nullptr, nullptr, 0, nullptr, nullptr);
+}
+
+// ---- fa_fwd_kvcache_noalloc: the decode workspace in a static device array.
+// In host code `scratch` is a host-side stand-in for the array, not a device
+// address: kernels are handed the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept in g_scratch_dev.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static std::atomic<void*> g_scratch_dev[kScratchDevices];
+static std::mutex g_scratch_mu;
+
+static fa_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(FA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev, kScratchDevices - 1);
+  void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return FA_OK;
+}
+
+size_t fa_kvcache_noalloc_max_bytes(void) { return kScratchBytes; }
+
+fa_status fa_fwd_kvcache_noalloc(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
+                                 const int* cache_seqlens, const int* block_table, int block_table_stride,
+                                 int page_size, int num_blocks_or_smax, int num_splits, void* out, float* lse,
+                                 int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream) {
+  fa_status st = check_common(dtype, Hq, Hkv, D);
+  if (st) return st;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  // sizes that describe work (the rest is validated, or is a no-op, in the shared path)
+  if (B > 0 && Sq > 0 && num_splits >= 0 && num_splits <= 64 && num_blocks_or_smax >= 0 &&
+      (!block_table || (page_size > 0 && block_table_stride > 0))) {
+    const int cap = block_table ? block_table_stride * page_size : num_blocks_or_smax;
+    const int ns = fa_kvcache_num_splits(B, Hkv, cap, num_splits);
+    const size_t need = fa_kvcache_workspace_size(B, Sq, Hq, D, ns);
+    if (need > kScratchBytes)
+      return fail(FA_ERR_UNSUPPORTED, "the decode needs %zu bytes of workspace; the static scratch holds %zu", need,
+                  kScratchBytes);
+    if ((st = scratch_of_current_device(&ws))) return st;
+    ws_bytes = kScratchBytes;
+  }
+  return kvcache_impl(dtype, q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), cache_seqlens, block_table,
+                      block_table_stride, page_size, num_blocks_or_smax, num_splits, ws, ws_bytes, out, lse, B, Sq,
+                      Hq, Hkv, D, opts, stream, nullptr, nullptr, 0, nullptr, nullptr);
 }
 
 fa_status fa_fwd_kvcache_append(fa_dtype dtype, const void* q, void* k_cache, void* v_cache,

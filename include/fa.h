@@ -201,6 +201,27 @@ fa_status fa_fwd_kvcache_append(fa_dtype dtype, const void* q, void* k_cache, vo
                                 int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream);
 
 /*
+ * fa_fwd_kvcache without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The decode partials live in a static device array of
+ * fa_kvcache_noalloc_max_bytes() bytes (32 MiB) that the library holds on every
+ * GPU it runs on until the process ends; the call allocates nothing and calls
+ * no allocating routine.  A call whose workspace (fa_kvcache_workspace_size for
+ * the resolved split count) exceeds that size returns FA_ERR_UNSUPPORTED with
+ * nothing launched.  All calls on one GPU share its array: calls that overlap
+ * in time on one GPU (other streams, other threads) race and give undefined
+ * results.  Nothing in the array needs clearing between calls: every partial
+ * the combine reads is written first by the same call.  Arguments, results and
+ * errors are otherwise those of fa_fwd_kvcache; the outputs equal its outputs
+ * bit for bit.
+ */
+size_t fa_kvcache_noalloc_max_bytes(void);
+fa_status fa_fwd_kvcache_noalloc(fa_dtype dtype, const void* q, const void* k_cache, const void* v_cache,
+                                 const int* cache_seqlens, const int* block_table, int block_table_stride,
+                                 int page_size, int num_blocks_or_smax, int num_splits, void* out, float* lse,
+                                 int B, int Sq, int Hq, int Hkv, int D, const fa_attn_opts* opts, void* stream);
+
+/*
  * Merge split partial results by their log-sum-exp ("FlashAttention 常用接口简单介绍",
  * §3.4 flash_attn_combine).  out_partial [B, S, H, D, num_splits] and
  * lse_partial [B, S, H, num_splits] float32; op_stride (5 entries: b, s, h, d,

@@ -325,3 +325,20 @@ def test_python_layer_checks_shapes_before_anything_runs():
         fa.combine(op, lp, out=_cpu(1, 1, 2, 32))
     with pytest.raises(ValueError, match="lse must be"):
         fa.combine(op, lp, lse=torch.zeros(1, 1, 3))
+
+
+def test_noalloc_rejects_beyond_its_static_workspace(lib):
+    """fa_fwd_kvcache_noalloc: a decode whose workspace exceeds the static array
+    is FA_ERR_UNSUPPORTED before anything touches the GPU; other errors are those
+    of fa_fwd_kvcache."""
+    ob, keep = _opts()
+    cap = lib.fa_kvcache_noalloc_max_bytes()
+    assert cap == 32 << 20
+    f = lambda B=64, Sq=1, Hq=32, Hkv=8, D=128, ns=64: lib.fa_fwd_kvcache_noalloc(
+        1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 256, 100, ns, FAKE, FAKE, B, Sq, Hq, Hkv, D, ob, None)
+    assert lib.fa_kvcache_workspace_size(64, 1, 32, 128, 64) > cap
+    assert f() == 2 and "static scratch" in lib.fa_last_error().decode()
+    assert f(D=80) == 2                     # head dim not built
+    assert f(Hq=30) == 1                    # Hkv must divide Hq
+    assert f(ns=-1) == 1
+    assert f(B=0) == 0                      # no work: nothing touched
