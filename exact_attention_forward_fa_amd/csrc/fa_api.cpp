@@ -236,6 +236,8 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
+  p.n_heads = B * Hq;
+  p.cus = device_cus();
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);
@@ -285,6 +287,8 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
   fill_opts(p, opts, scale * q_descale * k_descale);   // scores of the dequantised q and k
   p.out_scale = v_descale;
   p.n_qtiles = (int)nqt;
+  p.n_heads = B * Hq;
+  p.cus = device_cus();
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);
@@ -335,6 +339,8 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   p.B = B; p.Sq = max_seqlen_q; p.Sk = max_seqlen_k; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
+  p.n_heads = B * Hq;
+  p.cus = device_cus();
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);

@@ -24,6 +24,8 @@
 //  * scale·log2(e) is folded into the exp2 argument (one FMA + v_exp_f32 per score).
 //  * tiles that are fully masked for a wave are skipped; mask arithmetic runs only
 //    on tiles that straddle a mask edge.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -96,12 +98,13 @@ void prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
 
-  // ---- workgroup -> (batch, query head, query tile); heads are spread over the
-  // 8 XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
-  // within a head the longest (last) query tiles go first.
-  int id = blockIdx.x;
+  // ---- units (batch, query head, query tile); heads are spread over the 8
+  // XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
+  // within a head the longest (last) query tiles go first (tile_order).  A
+  // persistent grid walks them in rounds (persistent_unit).
+  for (int round = 0;; ++round) {
   int head, rank;
-  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.order_group, head, rank);
+  if (!persistent_unit(round, p, head, rank)) break;
   const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
@@ -114,7 +117,7 @@ void prefill_kernel(PrefillParams p) {
     sk = p.cu_seqlens_k[b + 1] - kbase;
   }
   const int m0 = qt * BM;
-  if (m0 >= sq) return;
+  if (m0 >= sq) continue;
 
   const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
   const TI* qp = (const TI*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
@@ -237,18 +240,16 @@ void prefill_kernel(PrefillParams p) {
   };
 
   f32x16 o[RB][DB];
-  // Running row max m (log2 units) and row sums over this lane's keys (the other
-  // half is added at the end): l of the rounded P that feeds the P V product
-  // (normalises out, so out is an exact convex combination of the rounded
-  // weights) and lx of the unrounded fp32 P (gives an lse free of P rounding).
-  // m is lazy (see step): O, l, lx are rescaled only when m moves, which leaves
-  // the result exact.
-  float m[RB], l[RB], lx[RB];
+  // Running row max m (log2 units) and row sum lx of the fp32 P over this lane's
+  // keys (the other half is added at the end).  lx normalises out and gives an
+  // lse free of the rounding of P; m is lazy (see step): O and lx are rescaled
+  // only when m moves, which leaves the result exact.
+  float m[RB], lx[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[rb][db] = f32x16{};
-    m[rb] = kNegInf; l[rb] = 0.f; lx[rb] = 0.f;
+    m[rb] = kNegInf; lx[rb] = 0.f;
   }
 
   // S^T = K Q^T for one tile: s[rb][kb][r] is key j0 + 32kb + 8(r/4) + 4hi + (r%4) of
@@ -306,13 +307,13 @@ void prefill_kernel(PrefillParams p) {
     }
   };
 
-  // P = exp2(s * mult - mu), rounded for the P V product, and this lane's sums of
-  // the rounded (ls) and unrounded (lxs) P of each row block
-  auto probs = [&](f32x16 (&s)[RB][KB], const float (&mu)[RB], V2 (&pk)[RB][KB][8], float (&ls)[RB],
+  // P = exp2(s * mult - mu), rounded for the P V product, and this lane's sum of
+  // the unrounded fp32 P (lxs) of each row block
+  auto probs = [&](f32x16 (&s)[RB][KB], const float (&mu)[RB], V2 (&pk)[RB][KB][8],
                    float (&lxs)[RB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float a = 0.f, ax = 0.f;
+      float ax = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -320,10 +321,8 @@ void prefill_kernel(PrefillParams p) {
           const float p0 = exp2_fast(fmaf(s[rb][kb][r], mult, -mu[rb]));
           const float p1 = exp2_fast(fmaf(s[rb][kb][r + 1], mult, -mu[rb]));
           pk[rb][kb][r >> 1] = E::pack(p0, p1);
-          a = E::sum2(pk[rb][kb][r >> 1], a);
           ax += p0 + p1;
         }
-      ls[rb] = a;
       lxs[rb] = ax;
     }
   };
@@ -338,14 +337,14 @@ void prefill_kernel(PrefillParams p) {
   auto step = [&](bool edge, int j0, const T* Ks, const T* Vs) __attribute__((always_inline)) {
     f32x16 s[RB][KB];
     V2 pk[RB][KB][8];
-    float ls[RB], lxs[RB];
+    float lxs[RB];
     bool unset = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) unset |= m[rb] == kNegInf;
     bool redo = true;
     if (!__any(unset)) {
       scores(edge, j0, Ks, s);
-      probs(s, m, pk, ls, lxs);
+      probs(s, m, pk, lxs);
       bool big = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) big |= lxs[rb] > kTauPow;
@@ -376,7 +375,6 @@ void prefill_kernel(PrefillParams p) {
         for (int rb = 0; rb < RB; ++rb) {
           const float alpha = mu[rb] == kNegInf ? 1.f : exp2_fast(m[rb] - mu[rb]);
           m[rb] = mu[rb];
-          l[rb] *= alpha;
           lx[rb] *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
@@ -384,13 +382,10 @@ void prefill_kernel(PrefillParams p) {
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) mu[rb] = m[rb] == kNegInf ? 0.f : m[rb];
-      probs(s, mu, pk, ls, lxs);
+      probs(s, mu, pk, lxs);
     }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      l[rb] += ls[rb];
-      lx[rb] += lxs[rb];
-    }
+    for (int rb = 0; rb < RB; ++rb) lx[rb] += lxs[rb];
 
     // O^T += V^T P^T over 16-key chunks; each V operand read feeds the RB blocks.
     // Transposing read: lane (g = lane % 16) of each 16-lane group addresses row
@@ -492,16 +487,13 @@ void prefill_kernel(PrefillParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: out = O / l, lse = ln(sum exp(scores)) = (m + log2 lx) * ln 2.
-  // norm: the row sum that normalises O (l of the rounded P, or lx after the
-  // precise pass, whose O is the product with P itself)
-  auto write_rows = [&](const float (&norm)[RB]) __attribute__((always_inline)) {
+  // ---- epilogue: out = O / lx, lse = ln(sum exp(scores)) = (m + log2 lx) * ln 2
+  auto write_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float lt = sum_halves(norm[rb]);
       const float lxt = sum_halves(lx[rb]);
       if (row_ok[rb]) {
-        const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
+        const float inv = lxt > 0.f ? p.out_scale / lxt : 0.f;
         T* orow = op + (int64_t)qrow[rb] * p.o_ss;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -526,7 +518,7 @@ void prefill_kernel(PrefillParams p) {
   bool need = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float lt = sum_halves(l[rb]);
+    const float lt = sum_halves(lx[rb]);
     float om = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -535,7 +527,7 @@ void prefill_kernel(PrefillParams p) {
     need |= row_ok[rb] && lt > 0.f && om * (p.out_scale / lt) >= kPreciseOut;
   }
   const bool wave_need = __any(need);
-  if (!wave_need) write_rows(l);
+  if (!wave_need) write_rows();
   if (__syncthreads_or(wave_need)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -563,8 +555,9 @@ void prefill_kernel(PrefillParams p) {
       if (t + 1 < t_hi) swrite(buf ^ 1);
       __syncthreads();
     }
-    if (wave_need) write_rows(lx);
+    if (wave_need) write_rows();
   }
+  }   // units
 }
 
 // ---------------------------------------------------------------------------
@@ -601,9 +594,9 @@ void prefill_pp_kernel(PrefillParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
 
-  int id = blockIdx.x;
+  for (int round = 0;; ++round) {
   int head, rank;
-  tile_order(id, (int)(gridDim.x / p.n_qtiles), p.n_qtiles, p.remap_xcd, p.order_group, head, rank);
+  if (!persistent_unit(round, p, head, rank)) break;
   const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
@@ -616,7 +609,7 @@ void prefill_pp_kernel(PrefillParams p) {
     sk = p.cu_seqlens_k[b + 1] - kbase;
   }
   const int m0 = qt * BM;
-  if (m0 >= sq) return;
+  if (m0 >= sq) continue;
 
   const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
   const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
@@ -696,7 +689,7 @@ void prefill_pp_kernel(PrefillParams p) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = kNegInf, l = 0.f, lx = 0.f;
+  float m = kNegInf, lx = 0.f;   // running row max (log2 units) and fp32 sum of P
   f32x16 s[KB];
   V2 pk[KB][8];
 
@@ -800,13 +793,12 @@ void prefill_pp_kernel(PrefillParams p) {
     if (__any(m_new > m + kTau)) {
       const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
       m = m_new;
-      l *= alpha;
       lx *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
     const float m_use = m == kNegInf ? 0.f : m;
-    float ls = 0.f, lxs = 0.f;
+    float lxs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -814,23 +806,19 @@ void prefill_pp_kernel(PrefillParams p) {
         const float p0 = exp2_fast(fmaf(s[kb][r], mult, -m_use));
         const float p1 = exp2_fast(fmaf(s[kb][r + 1], mult, -m_use));
         pk[kb][r >> 1] = E::pack(p0, p1);
-        ls = E::sum2(pk[kb][r >> 1], ls);
         lxs += p0 + p1;
       }
-    l += ls;
     lx += lxs;
     barrier();
     st_q = st_w;
   }
   if (grp == 0) barrier();                 // matches group 1's initial offset
 
-  // norm: the row sum that normalises O (l of the rounded P, or lx after the
-  // precise pass)
-  auto write_row = [&](float norm) __attribute__((always_inline)) {
-    const float lt = sum_halves(norm);
+  // out = O / lx, lse = (m + log2 lx) * ln 2
+  auto write_row = [&]() __attribute__((always_inline)) {
     const float lxt = sum_halves(lx);
     if (row_ok) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lxt > 0.f ? 1.f / lxt : 0.f;
       T* orow = op + (int64_t)qrow * p.o_ss;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -850,7 +838,7 @@ void prefill_pp_kernel(PrefillParams p) {
   // their row with P split into RN(P) and RN(P - RN(P)) against the final m.
   bool need = false;
   {
-    const float lt = sum_halves(l);
+    const float lt = sum_halves(lx);
     float om = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -859,7 +847,7 @@ void prefill_pp_kernel(PrefillParams p) {
     need = row_ok && lt > 0.f && om / lt >= kPreciseOut;
   }
   const bool wave_need = __any(need);
-  if (!wave_need) write_row(l);
+  if (!wave_need) write_row();
   if (__syncthreads_or(wave_need)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
@@ -920,8 +908,10 @@ void prefill_pp_kernel(PrefillParams p) {
         }
       }
     }
-    if (wave_need) write_row(lx);
+    barrier();                               // every wave is done with stage 0 before the next unit loads it
+    if (wave_need) write_row();
   }
+  }   // units
 }
 
 // Tile shapes: 8 waves of one 32-row block each, i.e. 256 query rows per
@@ -962,22 +952,48 @@ int prefill_block_m(int D, int64_t heads, int max_sq, int cus) {
   }
 }
 
+// Grid of a prefill launch: one workgroup per unit, or, when the units
+// outnumber the workgroups the device holds at once, a persistent grid of that
+// many (a multiple of 8 with the XCD mapping) that walks them in rounds.
+template <auto Kern>
+static unsigned prefill_grid(int threads, const PrefillParams& p) {
+  const int64_t total = (int64_t)p.n_qtiles * p.n_heads;
+  // resident workgroups per CU of this kernel (the same on every gfx950 device);
+  // computed once, and a concurrent first call at worst computes it twice
+  static std::atomic<int> cached{0};
+  int per_cu = cached.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, Kern, threads, 0) != hipSuccess || nb < 1) nb = 1;
+    per_cu = nb;
+    cached.store(nb, std::memory_order_relaxed);
+  }
+  int64_t slots = (int64_t)std::max(p.cus, 1) * per_cu;
+  if (p.remap_xcd) slots &= ~(int64_t)7;
+  if (slots < 8 || total <= slots) return (unsigned)total;
+  return (unsigned)slots;
+}
+
+template <auto Kern>
+static void launch_k(int threads, const PrefillParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(Kern, dim3(prefill_grid<Kern>(threads, p)), dim3(threads), 0, s, p);
+}
+
 template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
   using S = Shape<D>;
-  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
   if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128)) {
-    hipLaunchKernelGGL((prefill_pp_kernel<E, D, 64, SC, AL>), dim3(grid), dim3(512), 0, s, p);
+    launch_k<prefill_pp_kernel<E, D, 64, SC, AL>>(512, p, s);
   } else if constexpr (S::NW == 8 && S::RB == 1) {
     // fewer rows per workgroup when the grid would leave CUs idle (see prefill_block_m)
     if (p.block_m == 64)
-      hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, 2, 1, SC, AL>), dim3(grid), dim3(128), 0, s, p);
+      launch_k<prefill_kernel<E, D, S::BN, 2, 1, SC, AL>>(128, p, s);
     else if (p.block_m == 128)
-      hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, 4, 1, SC, AL>), dim3(grid), dim3(256), 0, s, p);
+      launch_k<prefill_kernel<E, D, S::BN, 4, 1, SC, AL>>(256, p, s);
     else
-      hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, 8, 1, SC, AL>), dim3(grid), dim3(512), 0, s, p);
+      launch_k<prefill_kernel<E, D, S::BN, 8, 1, SC, AL>>(512, p, s);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<E, D, S::BN, S::NW, S::RB, SC, AL>), dim3(grid), dim3(S::NW * 64), 0, s, p);
+    launch_k<prefill_kernel<E, D, S::BN, S::NW, S::RB, SC, AL>>(S::NW * 64, p, s);
   }
   return hipGetLastError();
 }
@@ -1007,8 +1023,7 @@ int prefill_block_m_fp8(int) { return 8 * 32; }
 
 template <int D, bool SC, bool AL>
 static hipError_t launch_f8(const PrefillParams& p, hipStream_t s) {
-  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.Hq * (unsigned)p.B;
-  hipLaunchKernelGGL((prefill_kernel<BF16, D, 64, 8, 1, SC, AL, true>), dim3(grid), dim3(512), 0, s, p);
+  launch_k<prefill_kernel<BF16, D, 64, 8, 1, SC, AL, true>>(512, p, s);
   return hipGetLastError();
 }
 
