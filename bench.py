@@ -17,7 +17,11 @@ k=, v=), "prefill_fp8" the prefill on the same inputs converted to fp8
 e4m3, and "backward" the gradients of that prefill (fa_bwd with a seeded
 dout, TFLOP/s at 10·D per allowed pair: the five products S, dP, dV, dK, dQ),
 all after the timed steps.  "cpu_baseline" times the float64 CPU oracle
-on a bounded sample of the prefill workload.
+on a bounded sample of the prefill workload.  "prefill_configs" times the
+other prefill workloads of the configurations (B1 S128 H2; B2 S1024 H8 causal,
+non-causal and packed; config 3's two windows; the B2 S8192 GQA bf16 case with
+softcap and ALiBi), each as TFLOP/s over its own allowed pairs and its fraction
+of the dense fp16/bf16 MFMA peak.
 """
 
 from __future__ import annotations
@@ -53,6 +57,22 @@ def causal_pairs(Sq: int, Sk: int) -> int:
     return total
 
 
+def allowed_pairs(Sq: int, Sk: int, causal: bool = False, window=(-1, -1)) -> int:
+    """Allowed (query, key) pairs of one head: bottom-right aligned causal mask and
+    inclusive window [i' - left, i' + right], i' = i + Sk - Sq (-1 = unbounded)."""
+    import numpy as np
+    ip = np.arange(Sq, dtype=np.int64) + (Sk - Sq)
+    lo = np.zeros(Sq, dtype=np.int64)
+    hi = np.full(Sq, Sk - 1, dtype=np.int64)
+    if window[0] >= 0:
+        lo = np.maximum(lo, ip - window[0])
+    if causal:
+        hi = np.minimum(hi, ip)
+    if window[1] >= 0:
+        hi = np.minimum(hi, ip + window[1])
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
 def kernel_source_hash(which: str = "prefill") -> str:
     """Short hash of the sources a kernel is built from; stored traffic figures
     are used only while it matches."""
@@ -76,7 +96,7 @@ def _oracle_head(args):
     return time.perf_counter() - t
 
 
-def cpu_baseline(case, n_heads: int, workers: int):
+def cpu_baseline(case, n_heads: int, workers: int, affinity: int):
     """Time the float64 oracle on n_heads (batch, head) pairs of the prefill workload."""
     import numpy as np
     q, k, v = case["q"], case["k"], case["v"]
@@ -95,8 +115,9 @@ def cpu_baseline(case, n_heads: int, workers: int):
     return dict(value=flops / wall / 1e12, unit="TFLOP/s", cores=workers, kind="oracle",
                 sample=f"float64 oracle, causal, {len(pairs)} of {B * H} (batch, head) pairs of the "
                        f"B{B} S{S} H{H} D{D} prefill, all {S} rows each, {workers} single-threaded "
-                       f"worker processes, {wall:.1f} s wall; FLOPs counted as 4·D per allowed pair; "
-                       f"CPU {cpu_model()}, numpy {np.__version__}",
+                       f"worker processes on {workers} of the {affinity} cores in this process's CPU "
+                       f"affinity (at most 16, the host share of one GPU), {wall:.1f} s wall; FLOPs "
+                       f"counted as 4·D per allowed pair; CPU {cpu_model()}, numpy {np.__version__}",
                 seconds=wall)
 
 
@@ -136,6 +157,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other configurations' prefill legs")
     ap.add_argument("--cpu-heads", type=int, default=128)
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one leg only (for profiling); the JSON line is still printed")
@@ -164,8 +186,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
-        cpu = cpu_baseline(pc, args.cpu_heads, workers)
+        affinity = len(os.sched_getaffinity(0))
+        workers = max(1, min(16, affinity))      # the host share of one GPU is 16 cores
+        cpu = cpu_baseline(pc, args.cpu_heads, workers, affinity)
         log(f"cpu baseline: {cpu['value']:.4f} TFLOP/s in {cpu['seconds']:.1f} s on {workers} cores")
 
     dev = torch.device("cuda:0")
@@ -283,6 +306,52 @@ def main():
         a_mean = sum(a_ms) / len(a_ms)
         a_bytes = d_bytes + 2 * 2 * kn.numel() * kn.element_size()   # new K/V read + cache rows written
 
+    # the other prefill workloads of the pages' configurations, timed the same way
+    legs = {}
+    if run_p and not args.no_extra:
+        def time_call(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                ev[i][0].record()
+                fn()
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            ms = [e[0].elapsed_time(e[1]) for e in ev]
+            return sum(ms) / len(ms)
+
+        for name in ("c1_noncausal", "c1_causal", "c1_decode", "c2_causal", "c2_noncausal", "c2_varlen",
+                     "c3_win256_0", "c3_win256_256", "c4_gqa"):
+            c = pc if name.startswith("c3") else inputs.case(name)
+            win = {"c3_win256_0": (256, 0), "c3_win256_256": (256, 256)}.get(name, c.get("window", (-1, -1)))
+            causal = {"c3_win256_0": True, "c3_win256_256": False}.get(name, c.get("causal", False))
+            xq, xk, xv = (c[n].to(dev) for n in ("q", "k", "v"))
+            slopes = c.get("alibi_slopes")
+            slopes = None if slopes is None else slopes.to(dev)
+            kw = dict(softmax_scale=c.get("softmax_scale"), causal=causal, window_size=win,
+                      softcap=c.get("softcap", 0.0), alibi_slopes=slopes)
+            if c["kind"] == "varlen":
+                cq, ck = c["cu_seqlens_q"].to(dev), c["cu_seqlens_k"].to(dev)
+                lens = (c["cu_seqlens_q"][1:] - c["cu_seqlens_q"][:-1]).tolist()
+                fl = 4 * xq.shape[-1] * xq.shape[1] * sum(allowed_pairs(n, n, causal, win) for n in lens)
+                ms = time_call(lambda: fa.fwd_varlen(xq, xk, xv, cq, ck, c["max_seqlen_q"], c["max_seqlen_k"], **kw))
+                shape = f"varlen lengths {lens} H{xq.shape[1]} D{xq.shape[2]}"
+            else:
+                Bq, Sq, Hq, Dq = xq.shape
+                fl = 4 * Dq * Hq * Bq * allowed_pairs(Sq, xk.shape[1], causal, win)
+                ms = time_call(lambda: fa.fwd(xq, xk, xv, **kw))
+                shape = f"B{Bq} Sq{Sq} Sk{xk.shape[1]} Hq{Hq} Hkv{xk.shape[2]} D{Dq}"
+            tf = fl / (ms * 1e-3) / 1e12
+            legs[name] = {"tflops": round(tf, 2), "frac": round(tf / PEAK_MFMA_F16_TFLOPS, 4), "ms_mean": round(ms, 5),
+                          "flops": fl, "dtype": str(xq.dtype).replace("torch.", ""),
+                          "shape": shape + (f", causal={causal}, window={win}" +
+                                            (f", softcap={kw['softcap']}" if kw["softcap"] else "") +
+                                            (", ALiBi" if slopes is not None else ""))}
+            log(f"{name}: {tf:.1f} TFLOP/s ({ms * 1e3:.1f} us)")
+            del xq, xk, xv
+
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -351,6 +420,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": None if cpu is None else {kk: cpu[kk] for kk in ("value", "unit", "cores", "kind", "sample")},
+        "prefill_configs": legs or None,
     }
     if cpu is not None:
         line["cpu_baseline"]["value"] = round(cpu["value"], 6)

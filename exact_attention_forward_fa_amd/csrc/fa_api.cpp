@@ -237,7 +237,6 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
   p.n_heads = B * Hq;
-  p.cus = device_cus();
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);
@@ -288,7 +287,6 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, flo
   p.out_scale = v_descale;
   p.n_qtiles = (int)nqt;
   p.n_heads = B * Hq;
-  p.cus = device_cus();
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);
@@ -340,7 +338,6 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   fill_opts(p, opts, scale);
   p.n_qtiles = (int)nqt;
   p.n_heads = B * Hq;
-  p.cus = device_cus();
   p.block_m = bm;
   p.remap_xcd = (((int64_t)Hq * B) % 8) == 0;
   p.order_group = fa::order_group(p.causal != 0, (int64_t)Hq * B, nqt, p.remap_xcd != 0);

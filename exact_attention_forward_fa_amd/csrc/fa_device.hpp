@@ -142,27 +142,6 @@ __device__ __forceinline__ void tile_order(int id, int n_units, int n_tiles, boo
   }
 }
 
-// Unit of round r for this workgroup.  A grid of n_heads * n_qtiles
-// workgroups takes one unit each in round 0 (workgroup id -> tile_order).  A
-// smaller, persistent grid of P workgroups (a multiple of 8 with the XCD
-// mapping) walks the same sequence of tile_order positions in rounds: on each
-// XCD its S slots take positions r*S + j in even rounds and r*S + S-1-j in odd
-// ones (snake order), so a slot that got one of the longest units in one round
-// gets one of the shortest in the next and every slot's total stays close to
-// the mean.  Returns false when the workgroup has no unit left.
-template <class Params>
-__device__ __forceinline__ bool persistent_unit(int r, const Params& p, int& head, int& rank) {
-  const int P = gridDim.x, w = blockIdx.x;
-  const bool xcd = p.remap_xcd;
-  const int S = xcd ? P >> 3 : P, j = xcd ? w >> 3 : w;
-  const int k = r * S + ((r & 1) ? S - 1 - j : j);
-  const int total = p.n_heads * p.n_qtiles;
-  const int vid = xcd ? (k << 3) + (w & 7) : k;
-  if (vid >= total) return false;
-  tile_order(vid, p.n_heads, p.n_qtiles, xcd, p.order_group, head, rank);
-  return true;
-}
-
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element (i % 4) of the 8-byte chunk addressed by lane
 // 4*j + i/4, for j = 0..3.

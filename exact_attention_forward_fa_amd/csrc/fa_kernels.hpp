@@ -33,8 +33,7 @@ struct PrefillParams {
   int causal;
   int wl, wr;                  // window (left, right), -1 = unbounded
   int n_qtiles;                // ceil(Sq / block_m)
-  int n_heads;                 // B * Hq: units are n_heads x n_qtiles (head, query tile) pairs
-  int cus;                     // compute units of the device (sizes a persistent grid)
+  int n_heads;                 // B * Hq: the grid is n_heads x n_qtiles (head, query tile) units
   int block_m;                 // query rows per workgroup (prefill_block_m)
   int remap_xcd;               // 1 when B*Hq is a multiple of 8: each XCD takes a contiguous eighth of the heads
   int order_group;             // heads per longest-first group (causal), 0 = head by head (see tile_order)

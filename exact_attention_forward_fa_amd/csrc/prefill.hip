@@ -24,8 +24,6 @@
 //  * scale·log2(e) is folded into the exp2 argument (one FMA + v_exp_f32 per score).
 //  * tiles that are fully masked for a wave are skipped; mask arithmetic runs only
 //    on tiles that straddle a mask edge.
-#include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -36,8 +34,16 @@ namespace fa {
 constexpr float kTau = 8.f;   // lazy-rescale threshold (log2 units)
 constexpr float kTauPow = 256.f;   // 2^kTau
 // |out| from which a wave recomputes its rows with P carried in two parts (see
-// the epilogue of prefill_kernel)
+// the epilogue of prefill_kernel).  Below it half an ulp of out leaves about
+// half of the error bar to the rounding of P.  prefill_kernel normalises O by
+// the fp32 sum of P, so rounding P perturbs out by up to u * sum_j w_j |v_j|
+// (u the unit roundoff of P's type), and the bar is |out| >= 1 for both types.
+// prefill_pp_kernel normalises by the sum of the rounded P, which makes out a
+// convex combination of the rounded weights and the perturbation
+// u * sum_j w_j |v_j - out|, smaller where |out| is large; there bf16 (half an
+// ulp 3.9e-3 under 2, against 8e-3) recomputes from 2.
 constexpr float kPreciseOut = 1.f;
+template <class E> constexpr float precise_out_pp() { return std::is_same_v<E, BF16> ? 2.f : 1.f; }
 
 // Head dims from which the ping-pong kernel is used.  With D = 64 the softmax
 // phase outweighs the MFMA phase and a single wave per SIMD cannot issue VALU
@@ -98,13 +104,11 @@ void prefill_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
 
-  // ---- units (batch, query head, query tile); heads are spread over the 8
-  // XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
-  // within a head the longest (last) query tiles go first (tile_order).  A
-  // persistent grid walks them in rounds (persistent_unit).
-  for (int round = 0;; ++round) {
+  // ---- workgroup -> (batch, query head, query tile); heads are spread over the
+  // 8 XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
+  // within a head the longest (last) query tiles go first.
   int head, rank;
-  if (!persistent_unit(round, p, head, rank)) break;
+  tile_order(blockIdx.x, p.n_heads, p.n_qtiles, p.remap_xcd, p.order_group, head, rank);
   const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
@@ -117,7 +121,7 @@ void prefill_kernel(PrefillParams p) {
     sk = p.cu_seqlens_k[b + 1] - kbase;
   }
   const int m0 = qt * BM;
-  if (m0 >= sq) continue;
+  if (m0 >= sq) return;
 
   const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
   const TI* qp = (const TI*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
@@ -557,7 +561,6 @@ void prefill_kernel(PrefillParams p) {
     }
     if (wave_need) write_rows();
   }
-  }   // units
 }
 
 // ---------------------------------------------------------------------------
@@ -594,9 +597,8 @@ void prefill_pp_kernel(PrefillParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
 
-  for (int round = 0;; ++round) {
   int head, rank;
-  if (!persistent_unit(round, p, head, rank)) break;
+  tile_order(blockIdx.x, p.n_heads, p.n_qtiles, p.remap_xcd, p.order_group, head, rank);
   const int qt = p.n_qtiles - 1 - rank;      // the last query tiles see the most keys under a causal mask
   const int b = head / p.Hq, hq = head - b * p.Hq;
   const int hk = hq / p.group;
@@ -609,7 +611,7 @@ void prefill_pp_kernel(PrefillParams p) {
     sk = p.cu_seqlens_k[b + 1] - kbase;
   }
   const int m0 = qt * BM;
-  if (m0 >= sq) continue;
+  if (m0 >= sq) return;
 
   const int64_t bq = p.cu_seqlens_q ? 0 : (int64_t)b;
   const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
@@ -689,7 +691,9 @@ void prefill_pp_kernel(PrefillParams p) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = kNegInf, lx = 0.f;   // running row max (log2 units) and fp32 sum of P
+  // running row max m (log2 units), sum l of the rounded P that feeds P V (it
+  // normalises out) and sum lx of the fp32 P (it gives lse)
+  float m = kNegInf, l = 0.f, lx = 0.f;
   f32x16 s[KB];
   V2 pk[KB][8];
 
@@ -793,12 +797,13 @@ void prefill_pp_kernel(PrefillParams p) {
     if (__any(m_new > m + kTau)) {
       const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
       m = m_new;
+      l *= alpha;
       lx *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
     const float m_use = m == kNegInf ? 0.f : m;
-    float lxs = 0.f;
+    float ls = 0.f, lxs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -806,19 +811,23 @@ void prefill_pp_kernel(PrefillParams p) {
         const float p0 = exp2_fast(fmaf(s[kb][r], mult, -m_use));
         const float p1 = exp2_fast(fmaf(s[kb][r + 1], mult, -m_use));
         pk[kb][r >> 1] = E::pack(p0, p1);
+        ls = E::sum2(pk[kb][r >> 1], ls);
         lxs += p0 + p1;
       }
+    l += ls;
     lx += lxs;
     barrier();
     st_q = st_w;
   }
   if (grp == 0) barrier();                 // matches group 1's initial offset
 
-  // out = O / lx, lse = (m + log2 lx) * ln 2
-  auto write_row = [&]() __attribute__((always_inline)) {
+  // out = O / norm (l, or lx after the precise pass, whose O is the product with
+  // P itself), lse = (m + log2 lx) * ln 2
+  auto write_row = [&](float norm) __attribute__((always_inline)) {
+    const float lt = sum_halves(norm);
     const float lxt = sum_halves(lx);
     if (row_ok) {
-      const float inv = lxt > 0.f ? 1.f / lxt : 0.f;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
       T* orow = op + (int64_t)qrow * p.o_ss;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -834,20 +843,20 @@ void prefill_pp_kernel(PrefillParams p) {
   };
 
   // The precise pass of prefill_kernel, here as a plain loop over one LDS stage:
-  // waves with an output element of magnitude kPreciseOut or more recompute
+  // waves with an output element of magnitude precise_out_pp<E>() or more recompute
   // their row with P split into RN(P) and RN(P - RN(P)) against the final m.
   bool need = false;
   {
-    const float lt = sum_halves(lx);
+    const float lt = sum_halves(l);
     float om = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) om = fmaxf(om, fabsf(o[db][r]));
-    need = row_ok && lt > 0.f && om / lt >= kPreciseOut;
+    need = row_ok && lt > 0.f && om / lt >= precise_out_pp<E>();
   }
   const bool wave_need = __any(need);
-  if (!wave_need) write_row();
+  if (!wave_need) write_row(l);
   if (__syncthreads_or(wave_need)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
@@ -908,10 +917,8 @@ void prefill_pp_kernel(PrefillParams p) {
         }
       }
     }
-    barrier();                               // every wave is done with stage 0 before the next unit loads it
-    if (wave_need) write_row();
+    if (wave_need) write_row(lx);
   }
-  }   // units
 }
 
 // Tile shapes: 8 waves of one 32-row block each, i.e. 256 query rows per
@@ -952,31 +959,11 @@ int prefill_block_m(int D, int64_t heads, int max_sq, int cus) {
   }
 }
 
-// Grid of a prefill launch: one workgroup per unit, or, when the units
-// outnumber the workgroups the device holds at once, a persistent grid of that
-// many (a multiple of 8 with the XCD mapping) that walks them in rounds.
-template <auto Kern>
-static unsigned prefill_grid(int threads, const PrefillParams& p) {
-  const int64_t total = (int64_t)p.n_qtiles * p.n_heads;
-  // resident workgroups per CU of this kernel (the same on every gfx950 device);
-  // computed once, and a concurrent first call at worst computes it twice
-  static std::atomic<int> cached{0};
-  int per_cu = cached.load(std::memory_order_relaxed);
-  if (per_cu == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, Kern, threads, 0) != hipSuccess || nb < 1) nb = 1;
-    per_cu = nb;
-    cached.store(nb, std::memory_order_relaxed);
-  }
-  int64_t slots = (int64_t)std::max(p.cus, 1) * per_cu;
-  if (p.remap_xcd) slots &= ~(int64_t)7;
-  if (slots < 8 || total <= slots) return (unsigned)total;
-  return (unsigned)slots;
-}
-
+// One workgroup per (head, query tile) unit.
 template <auto Kern>
 static void launch_k(int threads, const PrefillParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(Kern, dim3(prefill_grid<Kern>(threads, p)), dim3(threads), 0, s, p);
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.n_heads;
+  hipLaunchKernelGGL(Kern, dim3(grid), dim3(threads), 0, s, p);
 }
 
 template <class E, int D, bool SC, bool AL>

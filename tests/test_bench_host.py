@@ -31,3 +31,18 @@ def test_median_and_cpu_model():
     assert bench.median([3.0, 1.0, 2.0]) == 2.0
     assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+@pytest.mark.parametrize("sq,sk,causal,window", [
+    (4096, 4096, True, (256, 0)), (4096, 4096, False, (256, 256)), (300, 299, True, (-1, -1)),
+    (100, 37, False, (5, 3)), (37, 100, True, (10, -1)), (64, 64, False, (-1, -1)), (8, 8, False, (0, 0))])
+def test_allowed_pair_count_matches_oracle_mask(sq, sk, causal, window):
+    """The bench's pair counts (the FLOP denominators of every prefill leg) equal the
+    number of True entries of the oracle's mask, and the config 3 window counts
+    equal the closed forms 257*S - 256*257/2 and 513*S - 256*257."""
+    assert bench.allowed_pairs(sq, sk, causal, window) == int(
+        ref.allowed_mask(np.arange(sq), sq, sk, causal, window).sum())
+    if (sq, sk, causal, window) == (4096, 4096, True, (256, 0)):
+        assert bench.allowed_pairs(sq, sk, causal, window) == 257 * 4096 - 256 * 257 // 2
+    if (sq, sk, causal, window) == (4096, 4096, False, (256, 256)):
+        assert bench.allowed_pairs(sq, sk, causal, window) == 513 * 4096 - 256 * 257
