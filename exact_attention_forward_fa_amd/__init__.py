@@ -51,13 +51,21 @@ def library_path() -> str:
 
 
 def load_library():
-    """Load libfa.so (built by ``exact_attention_forward_fa_amd.build``)."""
+    """Load libfa.so (built by ``exact_attention_forward_fa_amd.build``), or the
+    library the environment variable FA_LIBRARY names (the debug builds)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m exact_attention_forward_fa_amd.build`")
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = bind_library(os.environ.get("FA_LIBRARY") or _LIB_PATH)
+    return _lib
+
+
+def bind_library(path: str):
+    """ctypes handle of a build of the library at path, with the argument types set
+    (load_library keeps one as the library every call uses)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m exact_attention_forward_fa_amd.build`")
+    lib = ctypes.CDLL(path)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     I64P = ctypes.POINTER(ctypes.c_int64)
     OP = ctypes.POINTER(_Opts)
@@ -93,7 +101,6 @@ def load_library():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

@@ -123,6 +123,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   __shared__ __attribute__((aligned(16))) T kbuf[C * KROW];
 
   const int lane = threadIdx.x, n = lane & 15, q4 = lane >> 4;
+  lds_poison(vbuf, sizeof(vbuf), lane, 64);
+  lds_poison(kbuf, sizeof(kbuf), lane, 64);
   const int lpc = lane % CHP;             // this lane's piece of its row
   const bool piece_ok = CH == CHP || lpc < CH;
   const int lcol = piece_ok ? lpc : 0;    // the piece it loads

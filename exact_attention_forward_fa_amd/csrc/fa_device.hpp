@@ -142,6 +142,21 @@ __device__ __forceinline__ void tile_order(int id, int n_units, int n_tiles, boo
   }
 }
 
+// Debug build (FA_LDS_POISON=1): fill an LDS staging buffer with all-ones bits
+// (NaN in fp16, bf16 and fp32) and wait for the whole workgroup, before any tile
+// is stored.  A read that a missing wait or barrier lets run ahead of its tile's
+// store then carries NaN into the output.  The ordinary build does nothing.
+#ifndef FA_LDS_POISON
+#define FA_LDS_POISON 0
+#endif
+__device__ __forceinline__ void lds_poison(void* lds, size_t bytes, int tid, int nthreads) {
+  if constexpr (FA_LDS_POISON) {
+    uint32_t* w = static_cast<uint32_t*>(lds);
+    for (size_t i = tid; i < bytes / 4; i += nthreads) w[i] = 0xffffffffu;
+    __syncthreads();
+  }
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element (i % 4) of the 8-byte chunk addressed by lane
 // 4*j + i/4, for j = 0..3.

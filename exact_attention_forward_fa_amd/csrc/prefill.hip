@@ -103,6 +103,8 @@ void prefill_kernel(PrefillParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
+  lds_poison(ksm, sizeof(ksm), tid, NT);
+  lds_poison(vsm, sizeof(vsm), tid, NT);
 
   // ---- workgroup -> (batch, query head, query tile); heads are spread over the
   // 8 XCDs in contiguous ranges so the workgroups sharing K/V share an L2, and
@@ -596,6 +598,8 @@ void prefill_pp_kernel(PrefillParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
+  lds_poison(ksm, sizeof(ksm), tid, NT);
+  lds_poison(vsm, sizeof(vsm), tid, NT);
 
   int head, rank;
   tile_order(blockIdx.x, p.n_heads, p.n_qtiles, p.remap_xcd, p.order_group, head, rank);

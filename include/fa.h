@@ -56,7 +56,14 @@ typedef enum {
   FA_ERR_HIP = 4                 /* a HIP launch error; fa_last_error() carries its text */
 } fa_status;
 
-typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+typedef enum {
+  FA_F16 = 0,
+  FA_BF16 = 1,
+  /* range markers (not types): they make every int32 value a valid fa_dtype, so
+   * an unknown code is reported as FA_ERR_INVALID_ARGUMENT, never undefined */
+  FA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  FA_DTYPE_RANGE_MAX_ = 0x7fffffff
+} fa_dtype;
 
 /* Attention options ("FlashAttention 常用接口简单介绍", §3.1 keyword arguments). */
 typedef struct {
