@@ -293,24 +293,33 @@ void bwd_dkdv_kernel(BackwardParams p) {
     }
     V8 pa[2], sa[2];
     const float dist0 = (float)(i0 + 4 * hi + shift - j);
+    // P for all 16 registers, then the mask of an edge block under one uniform
+    // branch (a per-element test made the compiler branch on every element),
+    // then dS and the packs
+    float pv[16], dcap[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int qo = 8 * (rr >> 2) + (rr & 3);
+      const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 + (float)qo, sl2, cap_in, cap_l2, slope_l2, dcap[rr]);
+      pv[rr] = exp2_fast(x - L[rr >> 2][rr & 3]);
+    }
+    if (edge) {
+      const int ilo = a_j - i0 - 4 * hi, ihi = b_j - i0 - 4 * hi;   // allowed row offsets
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int qo = 8 * (rr >> 2) + (rr & 3);
+        if (qo < ilo || qo > ihi) pv[rr] = 0.f;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float pr[2], ds[2];
+      float ds[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
-        const int qo = 8 * (rr >> 2) + (rr & 3);
-        float dcap;
-        const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 + (float)qo, sl2, cap_in, cap_l2, slope_l2, dcap);
-        float pv = exp2_fast(x - L[rr >> 2][rr & 3]);
-        if (edge) {
-          const int i = i0 + 4 * hi + qo;
-          if (i < a_j || i > b_j) pv = 0.f;
-        }
-        pr[u] = pv;
-        ds[u] = DO_DK ? pv * (dp[rr] - Dl[rr >> 2][rr & 3]) * dcap : 0.f;
+        ds[u] = DO_DK ? pv[rr] * (dp[rr] - Dl[rr >> 2][rr & 3]) * dcap[rr] : 0.f;
       }
-      const V2 pp = E::pack(pr[0], pr[1]);
+      const V2 pp = E::pack(pv[r], pv[r + 1]);
       const V2 sp = E::pack(ds[0], ds[1]);
       pa[r >> 3][r & 7] = pp[0];
       pa[r >> 3][(r & 7) + 1] = pp[1];
@@ -503,21 +512,29 @@ void bwd_dq_kernel(BackwardParams p) {
     // register r holds key j0 + 8(r/4) + 4hi + r%4 for the lane's query
     V8 sa[2];
     const float dist0 = (float)(ip - j0 - 4 * hi);
+    // P for all 16 registers, the edge mask under one uniform branch, then dS
+    float pv[16], dcap[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int ko = 8 * (rr >> 2) + (rr & 3);
+      const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 - (float)ko, sl2, cap_in, cap_l2, slope_l2, dcap[rr]);
+      pv[rr] = exp2_fast(x - L);
+    }
+    if (edge) {
+      const int jlo = j_lo - j0 - 4 * hi, jhi = j_hi - j0 - 4 * hi;   // allowed key offsets
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int ko = 8 * (rr >> 2) + (rr & 3);
+        if (ko < jlo || ko > jhi) pv[rr] = 0.f;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       float ds[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
-        const int ko = 8 * (rr >> 2) + (rr & 3);
-        float dcap;
-        const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 - (float)ko, sl2, cap_in, cap_l2, slope_l2, dcap);
-        float pv = exp2_fast(x - L);
-        if (edge) {
-          const int jj = j0 + 4 * hi + ko;
-          if (jj < j_lo || jj > j_hi) pv = 0.f;
-        }
-        ds[u] = pv * (dp[rr] - Dl) * dcap;
+        ds[u] = pv[rr] * (dp[rr] - Dl) * dcap[rr];
       }
       const V2 sp = E::pack(ds[0], ds[1]);
       sa[r >> 3][r & 7] = sp[0];
