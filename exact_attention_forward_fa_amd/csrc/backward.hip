@@ -160,7 +160,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
   __shared__ __attribute__((aligned(16))) T qsm[2][BMQ * D];
   __shared__ __attribute__((aligned(16))) T gsm[2][BMQ * D];     // dO
   __shared__ __attribute__((aligned(16))) float lsm[2][BMQ];     // lse in log2 units; +inf: row adds nothing
-  __shared__ __attribute__((aligned(16))) float esm[2][BMQ];     // delta
+  __shared__ __attribute__((aligned(16))) float esm[2][BMQ];     // -delta
   __shared__ __attribute__((aligned(16))) T vsm[V_LDS ? NW * 32 * D : 8];   // V rows of each wave's keys
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -243,7 +243,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
       const float l = p.lse[bq * p.lse_sb + (int64_t)hq * p.lse_sh + qbase + rc];
       const float d = p.delta[bq * p.dl_sb + (int64_t)hq * p.dl_sh + qbase + rc];
       lst = (row < sq && l != kNegInf) ? l * kLog2e : __builtin_inff();
-      est = row < sq ? d : 0.f;
+      est = row < sq ? -d : 0.f;   // -delta: it starts the dP accumulation
     }
   };
   auto swrite = [&](int buf) __attribute__((always_inline)) {
@@ -276,7 +276,18 @@ void bwd_dkdv_kernel(BackwardParams p) {
   // the wave's 32 keys
   auto block = [&](const T* qs, const T* gs, const float* ls, const float* es, int rb0, int i0, bool edge,
                    float slope_l2) __attribute__((always_inline)) {
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // register r of s holds query row rb0 + 8(r/4) + 4hi + r%4 for the lane's key;
+    // dp starts from -delta of those rows, so it ends as dP - delta
+    f32x4 L[4];
+    f32x16 dp;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      L[t] = *(const f32x4*)(ls + rb0 + 8 * t + 4 * hi);
+      const f32x4 nd = *(const f32x4*)(es + rb0 + 8 * t + 4 * hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * t + e] = nd[e];
+    }
+    f32x16 s = f32x16{};
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       const int off = swz<D>(rb0 + l32, 2 * dc + hi);
@@ -284,47 +295,46 @@ void bwd_dkdv_kernel(BackwardParams p) {
       if constexpr (V_LDS) dp = E::mfma32(*(const V8*)(gs + off), *(const V8*)(vw + swz<D>(l32, 2 * dc + hi)), dp);
       else if constexpr (DO_DK) dp = E::mfma32(*(const V8*)(gs + off), vr[dc], dp);
     }
-    // register r of s holds query row rb0 + 8(r/4) + 4hi + r%4 for the lane's key
-    f32x4 L[4], Dl[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      L[t] = *(const f32x4*)(ls + rb0 + 8 * t + 4 * hi);
-      Dl[t] = *(const f32x4*)(es + rb0 + 8 * t + 4 * hi);
-    }
     V8 pa[2], sa[2];
     const float dist0 = (float)(i0 + 4 * hi + shift - j);
-    // P for all 16 registers, then the mask of an edge block under one uniform
-    // branch (a per-element test made the compiler branch on every element),
-    // then dS and the packs
-    float pv[16], dcap[16];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int qo = 8 * (rr >> 2) + (rr & 3);
-      const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 + (float)qo, sl2, cap_in, cap_l2, slope_l2, dcap[rr]);
-      pv[rr] = exp2_fast(x - L[rr >> 2][rr & 3]);
-    }
-    if (edge) {
-      const int ilo = a_j - i0 - 4 * hi, ihi = b_j - i0 - 4 * hi;   // allowed row offsets
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int qo = 8 * (rr >> 2) + (rr & 3);
-        if (qo < ilo || qo > ihi) pv[rr] = 0.f;
-      }
-    }
+    // P and dS of every register, packed; then, in an edge block only, the
+    // masked halves of the packed words are cleared under one uniform branch (a
+    // mask test per element made the compiler branch on the edge flag at every
+    // element).  Cleared bits are +0 whatever P was computed there.
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float ds[2];
+      float pr[2], ds[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
-        ds[u] = DO_DK ? pv[rr] * (dp[rr] - Dl[rr >> 2][rr & 3]) * dcap[rr] : 0.f;
+        const int qo = 8 * (rr >> 2) + (rr & 3);
+        float dcap;
+        const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 + (float)qo, sl2, cap_in, cap_l2, slope_l2, dcap);
+        pr[u] = exp2_fast(x - L[rr >> 2][rr & 3]);
+        ds[u] = DO_DK ? pr[u] * dp[rr] * dcap : 0.f;
       }
-      const V2 pp = E::pack(pv[r], pv[r + 1]);
+      const V2 pp = E::pack(pr[0], pr[1]);
       const V2 sp = E::pack(ds[0], ds[1]);
       pa[r >> 3][r & 7] = pp[0];
       pa[r >> 3][(r & 7) + 1] = pp[1];
       sa[r >> 3][r & 7] = sp[0];
       sa[r >> 3][(r & 7) + 1] = sp[1];
+    }
+    if (edge) {
+      const int ilo = a_j - i0 - 4 * hi, ihi = b_j - i0 - 4 * hi;   // allowed row offsets
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 pw = __builtin_bit_cast(u32x4, pa[h]), sw = __builtin_bit_cast(u32x4, sa[h]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r = 8 * h + 2 * w, q0 = 8 * (r >> 2) + (r & 3);   // rows of registers r, r+1
+          const uint32_t keep = (q0 < ilo || q0 > ihi ? 0u : 0xffffu) | (q0 + 1 < ilo || q0 + 1 > ihi ? 0u : 0xffff0000u);
+          pw[w] &= keep;
+          sw[w] &= keep;
+        }
+        pa[h] = __builtin_bit_cast(V8, pw);
+        sa[h] = __builtin_bit_cast(V8, sw);
+      }
     }
     // dV += Pᵀ dO and dK += dSᵀ Q over two 16-query chunks; the contraction order
     // inside a chunk is the register order of P, matched by the transposing read
@@ -512,33 +522,36 @@ void bwd_dq_kernel(BackwardParams p) {
     // register r holds key j0 + 8(r/4) + 4hi + r%4 for the lane's query
     V8 sa[2];
     const float dist0 = (float)(ip - j0 - 4 * hi);
-    // P for all 16 registers, the edge mask under one uniform branch, then dS
-    float pv[16], dcap[16];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int ko = 8 * (rr >> 2) + (rr & 3);
-      const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 - (float)ko, sl2, cap_in, cap_l2, slope_l2, dcap[rr]);
-      pv[rr] = exp2_fast(x - L);
-    }
-    if (edge) {
-      const int jlo = j_lo - j0 - 4 * hi, jhi = j_hi - j0 - 4 * hi;   // allowed key offsets
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int ko = 8 * (rr >> 2) + (rr & 3);
-        if (ko < jlo || ko > jhi) pv[rr] = 0.f;
-      }
-    }
+    // dS of every register, packed; in an edge block the masked halves are then
+    // cleared under one uniform branch (see bwd_dkdv_kernel)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       float ds[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rr = r + u;
-        ds[u] = pv[rr] * (dp[rr] - Dl) * dcap[rr];
+        const int ko = 8 * (rr >> 2) + (rr & 3);
+        float dcap;
+        const float x = score_l2<SOFTCAP, ALIBI>(s[rr], dist0 - (float)ko, sl2, cap_in, cap_l2, slope_l2, dcap);
+        const float pv = exp2_fast(x - L);
+        ds[u] = pv * (dp[rr] - Dl) * dcap;
       }
       const V2 sp = E::pack(ds[0], ds[1]);
       sa[r >> 3][r & 7] = sp[0];
       sa[r >> 3][(r & 7) + 1] = sp[1];
+    }
+    if (edge) {
+      const int jlo = j_lo - j0 - 4 * hi, jhi = j_hi - j0 - 4 * hi;   // allowed key offsets
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 sw = __builtin_bit_cast(u32x4, sa[h]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r = 8 * h + 2 * w, k0 = 8 * (r >> 2) + (r & 3);   // keys of registers r, r+1
+          sw[w] &= (k0 < jlo || k0 > jhi ? 0u : 0xffffu) | (k0 + 1 < jlo || k0 + 1 > jhi ? 0u : 0xffff0000u);
+        }
+        sa[h] = __builtin_bit_cast(V8, sw);
+      }
     }
     // dQ += dS K over two 16-key chunks, K read transposed
 #pragma unroll
