@@ -31,6 +31,7 @@
 // Both streaming kernels hold their LDS tiles in an XOR-swizzled row-major
 // layout (swz below) that serves the plain 16-byte operand reads and the
 // transposing reads without bank conflicts.
+#include <type_traits>
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -364,8 +365,10 @@ void bwd_dkdv_kernel(BackwardParams p) {
     swrite(0);
   }
   __syncthreads();
-  for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
+  // one step per query tile; the loop is unrolled by the two LDS buffers, so
+  // every LDS address is a per-lane base plus an immediate
+  auto step = [&](int it, auto Buf) __attribute__((always_inline)) {
+    constexpr int buf = decltype(Buf)::value;
     if (it + 1 < total) gload(it + 1);
     const int g = it / nt, t = t_lo + (it - g * nt);
     const int hq = hk * p.group + g;
@@ -380,6 +383,10 @@ void bwd_dkdv_kernel(BackwardParams p) {
     }
     if (it + 1 < total) swrite(buf ^ 1);
     __syncthreads();
+  };
+  for (int it = 0; it < total; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < total) step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: register r of dk[db] / dv[db] is key n0 + 32w + 8(r/4) + 4hi + r%4,
@@ -572,8 +579,9 @@ void bwd_dq_kernel(BackwardParams p) {
     swrite(0);
   }
   __syncthreads();
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
+  // one step per key tile, unrolled by the two LDS buffers (see bwd_dkdv_kernel)
+  auto step = [&](int t, auto Buf) __attribute__((always_inline)) {
+    constexpr int buf = decltype(Buf)::value;
     if (t + 1 < t_hi) gload(t + 1);
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -585,6 +593,10 @@ void bwd_dq_kernel(BackwardParams p) {
     }
     if (t + 1 < t_hi) swrite(buf ^ 1);
     __syncthreads();
+  };
+  for (int t = t_lo; t < t_hi; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < t_hi) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: register r of dq[db] is query m0 + 32w + 8(r/4) + 4hi + r%4, d = 32db + l32
