@@ -225,18 +225,40 @@ void bwd_dkdv_kernel(BackwardParams p) {
   // clamped to a real row and get lse = +inf, so their P is 0)
   u32x4 qst[LQ], gst[LQ];
   float lst = 0.f, est = 0.f;
+  // a whole tile is read as a wave-uniform tile base plus a fixed 32-bit byte
+  // offset per lane when a tile's rows span less than 2 GiB; the last, partial
+  // tile (and huge strides) clamp row by row
+  const bool off32 = (int64_t)BMQ * (p.q_ss > p.do_ss ? p.q_ss : p.do_ss) * (int64_t)sizeof(T) < ((int64_t)1 << 31) &&
+                     p.q_ss >= 0 && p.do_ss >= 0;
+  uint32_t qoff[LQ], goff[LQ];
+#pragma unroll
+  for (int i = 0; i < LQ; ++i) {
+    const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+    qoff[i] = off32 ? (uint32_t)(((int64_t)r * p.q_ss + c * 8) * (int64_t)sizeof(T)) : 0u;
+    goff[i] = off32 ? (uint32_t)(((int64_t)r * p.do_ss + c * 8) * (int64_t)sizeof(T)) : 0u;
+  }
   auto gload = [&](int it) __attribute__((always_inline)) {
     const int g = it / nt, t = t_lo + (it - g * nt);
     const int hq = hk * p.group + g;
     const int r0 = t * BMQ;
     const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)qbase * p.q_ss + (int64_t)hq * p.q_sh;
     const T* gp = (const T*)p.dout + bq * p.do_sb + (int64_t)qbase * p.do_ss + (int64_t)hq * p.do_sh;
+    if (off32 && r0 + BMQ <= sq) {
+      const char* qt = (const char*)(qp + (int64_t)r0 * p.q_ss);
+      const char* gt = (const char*)(gp + (int64_t)r0 * p.do_ss);
 #pragma unroll
-    for (int i = 0; i < LQ; ++i) {
-      const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
-      const int row = min(r0 + r, sq - 1);
-      qst[i] = *(const u32x4*)(qp + (int64_t)row * p.q_ss + c * 8);
-      gst[i] = *(const u32x4*)(gp + (int64_t)row * p.do_ss + c * 8);
+      for (int i = 0; i < LQ; ++i) {
+        qst[i] = *(const u32x4*)(qt + qoff[i]);
+        gst[i] = *(const u32x4*)(gt + goff[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LQ; ++i) {
+        const int cid = tid + i * NT, r = cid / CH, c = cid - r * CH;
+        const int row = min(r0 + r, sq - 1);
+        qst[i] = *(const u32x4*)(qp + (int64_t)row * p.q_ss + c * 8);
+        gst[i] = *(const u32x4*)(gp + (int64_t)row * p.do_ss + c * 8);
+      }
     }
     if (tid < BMQ) {
       const int row = r0 + tid;
@@ -491,13 +513,38 @@ void bwd_dq_kernel(BackwardParams p) {
   const T* kp = (const T*)p.k + bq * p.k_sb + (int64_t)kbase * p.k_ss + (int64_t)hk * p.k_sh;
   const T* vp = (const T*)p.v + bq * p.v_sb + (int64_t)kbase * p.v_ss + (int64_t)hk * p.v_sh;
   u32x4 kst[LK], vst[LK];
-  auto gload = [&](int t) __attribute__((always_inline)) {
+  // whole tiles: a uniform tile base plus a fixed 32-bit byte offset per lane
+  // (see bwd_dkdv_kernel); the last, partial tile clamps row by row.  Not at
+  // D = 64 with softcap or ALiBi, where the offsets' registers spill at the
+  // budget of three waves per SIMD.
+  constexpr bool kOff32 = D != 64 || !(SOFTCAP || ALIBI);
+  const bool off32 = kOff32 &&
+                     (int64_t)BN * (p.k_ss > p.v_ss ? p.k_ss : p.v_ss) * (int64_t)sizeof(T) < ((int64_t)1 << 31) &&
+                     p.k_ss >= 0 && p.v_ss >= 0;
+  uint32_t koff[LK], voff[LK];
 #pragma unroll
-    for (int u = 0; u < LK; ++u) {
-      const int cid = tid + u * NT, r = cid / CH, c = cid - r * CH;
-      const int row = min(t * BN + r, sk - 1);
-      kst[u] = *(const u32x4*)(kp + (int64_t)row * p.k_ss + c * 8);
-      vst[u] = *(const u32x4*)(vp + (int64_t)row * p.v_ss + c * 8);
+  for (int u = 0; u < LK; ++u) {
+    const int cid = tid + u * NT, r = cid / CH, c = cid - r * CH;
+    koff[u] = off32 ? (uint32_t)(((int64_t)r * p.k_ss + c * 8) * (int64_t)sizeof(T)) : 0u;
+    voff[u] = off32 ? (uint32_t)(((int64_t)r * p.v_ss + c * 8) * (int64_t)sizeof(T)) : 0u;
+  }
+  auto gload = [&](int t) __attribute__((always_inline)) {
+    if (off32 && (t + 1) * BN <= sk) {
+      const char* kt = (const char*)(kp + (int64_t)(t * BN) * p.k_ss);
+      const char* vt = (const char*)(vp + (int64_t)(t * BN) * p.v_ss);
+#pragma unroll
+      for (int u = 0; u < LK; ++u) {
+        kst[u] = *(const u32x4*)(kt + koff[u]);
+        vst[u] = *(const u32x4*)(vt + voff[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < LK; ++u) {
+        const int cid = tid + u * NT, r = cid / CH, c = cid - r * CH;
+        const int row = min(t * BN + r, sk - 1);
+        kst[u] = *(const u32x4*)(kp + (int64_t)row * p.k_ss + c * 8);
+        vst[u] = *(const u32x4*)(vp + (int64_t)row * p.v_ss + c * 8);
+      }
     }
   };
   auto swrite = [&](int buf) __attribute__((always_inline)) {
