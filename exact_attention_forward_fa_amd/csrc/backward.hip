@@ -108,16 +108,22 @@ constexpr int kBig = 1 << 30;
 
 // Workgroup shapes and register budgets (waves per SIMD the compiler targets).
 #ifndef FA_BWD_KV_NW64
-#define FA_BWD_KV_NW64 4
+#define FA_BWD_KV_NW64 8
 #endif
 #ifndef FA_BWD_KV_WPE64
 #define FA_BWD_KV_WPE64 2
+#endif
+#ifndef FA_BWD_KV_NW96
+#define FA_BWD_KV_NW96 4
 #endif
 #ifndef FA_BWD_KV_NW128
 #define FA_BWD_KV_NW128 4
 #endif
 #ifndef FA_BWD_KV_BMQ64
-#define FA_BWD_KV_BMQ64 64
+#define FA_BWD_KV_BMQ64 128
+#endif
+#ifndef FA_BWD_KV_BMQ96
+#define FA_BWD_KV_BMQ96 64
 #endif
 #ifndef FA_BWD_KV_BMQ128
 #define FA_BWD_KV_BMQ128 64
@@ -152,7 +158,7 @@ void bwd_dkdv_kernel(BackwardParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
   using V2 = typename E::V2;
-  constexpr int BMQ = V_LDS ? 32 : D >= 128 ? FA_BWD_KV_BMQ128 : FA_BWD_KV_BMQ64;   // query rows per LDS tile
+  constexpr int BMQ = V_LDS ? 32 : D >= 128 ? FA_BWD_KV_BMQ128 : D >= 96 ? FA_BWD_KV_BMQ96 : FA_BWD_KV_BMQ64;   // query rows per LDS tile
   constexpr int BNK = NW * 32;            // keys per workgroup
   constexpr int CH = D / 8, DC = D / 16, DB = D / 32;
   constexpr int NT = NW * 64;
@@ -661,10 +667,10 @@ void bwd_dq_kernel(BackwardParams p) {
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <int D> constexpr int bwd_dkdv_waves() { return D >= 128 ? FA_BWD_KV_NW128 : FA_BWD_KV_NW64; }
+template <int D> constexpr int bwd_dkdv_waves() { return D >= 128 ? FA_BWD_KV_NW128 : D >= 96 ? FA_BWD_KV_NW96 : FA_BWD_KV_NW64; }
 template <int D> constexpr int bwd_dq_waves() { return D >= 256 ? 4 : D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64; }
 
-int backward_block_n(int D) { return (D >= 128 ? FA_BWD_KV_NW128 : FA_BWD_KV_NW64) * 32; }
+int backward_block_n(int D) { return (D >= 128 ? FA_BWD_KV_NW128 : D >= 96 ? FA_BWD_KV_NW96 : FA_BWD_KV_NW64) * 32; }
 int backward_block_m(int D) { return (D >= 256 ? 4 : D >= 128 ? FA_BWD_Q_NW128 : FA_BWD_Q_NW64) * 32; }
 
 template <class E, int D, bool SOFTCAP, bool ALIBI>
