@@ -23,7 +23,8 @@ non-causal and packed; config 3's two windows; the B2 S8192 GQA bf16 case with
 softcap and ALiBi), each as TFLOP/s over its own allowed pairs and its fraction
 of the dense fp16/bf16 MFMA peak, from a HIP graph of back-to-back calls (the
 small configurations' kernels take less time than a Python call); the best of
-three replays.
+three replays.  By default 10 untimed warm-up steps precede 100 timed ones,
+and every leg reports the mean (and the main legs the median and minimum).
 """
 
 from __future__ import annotations
@@ -156,8 +157,8 @@ def decode_bytes(c) -> int:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)    # timed steps (10 warm-up + 100 timed by default)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations' prefill legs")
     ap.add_argument("--cpu-heads", type=int, default=128)
