@@ -262,6 +262,35 @@ def test_backward_strided_views_equal_contiguous():
         assert torch.equal(x, y)
 
 
+def test_huge_sequence_stride_equals_contiguous():
+    """q, k, v and dout with a sequence stride of 2^23 + 256 elements: a 128-row
+    tile then spans more than 2 GiB, so the forward and both backward kernels
+    take their row-by-row address path on every tile instead of the 32-bit
+    per-lane offsets; the bits equal those of contiguous copies."""
+    print("case huge sequence stride", flush=True)
+    B, S, H, D = 1, 130, 2, 64
+    ss = (1 << 23) + 256
+    gen = torch.Generator().manual_seed(4750)
+    small = [inputs.randn(gen, (B, S, H, D), torch.float16) for _ in range(4)]
+    views = []
+    for t in small:
+        store = torch.zeros(B * S * ss, dtype=torch.float16, device=DEV)
+        v = store.as_strided((B, S, H, D), (S * ss, ss, D, 1))
+        v.copy_(t.to(DEV))
+        views.append(v)
+    q, k, v, dout = views
+    assert q.stride(1) == ss
+    out, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(dout, q, k, v, out, lse, causal=True)
+    qc, kc, vc, dc = (t.to(DEV) for t in small)
+    out2, lse2 = fa.fwd(qc, kc, vc, causal=True)
+    b = fa.bwd(dc, qc, kc, vc, out2, lse2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 # ---------------------------------------------------------------- full sizes, sampled heads
 
 @pytest.mark.parametrize("name,heads", [("c3_causal", [(1, 7), (3, 30)]), ("c4_gqa", [(1, 5)])])
