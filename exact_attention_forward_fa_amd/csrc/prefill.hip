@@ -301,13 +301,17 @@ void prefill_kernel(PrefillParams p) {
           }
       }
       if (edge) {
-        const int jb = j0 + 4 * hi;
+        // key j is kept iff j_lo <= j <= j_hi, i.e. iff j - j_lo, taken unsigned,
+        // is below the row's key count (0 for a row without keys): one add, one
+        // compare and one select per score
+        const int base = j0 + 4 * hi - j_lo[rb];
+        const uint32_t cnt = (uint32_t)max(j_hi[rb] - j_lo[rb] + 1, 0);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = jb + kb * 32 + (r >> 2) * 8 + (r & 3);
-            if (j < j_lo[rb] || j > j_hi[rb]) s[rb][kb][r] = kNegInf;
+            const uint32_t x = (uint32_t)(base + kb * 32 + (r >> 2) * 8 + (r & 3));
+            if (x >= cnt) s[rb][kb][r] = kNegInf;
           }
       }
     }
@@ -782,13 +786,15 @@ void prefill_pp_kernel(PrefillParams p) {
         }
     }
     if (edge) {
-      const int jb = j0 + 4 * hi;
+      // one unsigned compare per score, as in prefill_kernel
+      const int base = j0 + 4 * hi - j_lo;
+      const uint32_t cnt = (uint32_t)max(j_hi - j_lo + 1, 0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int jj = jb + kb * 32 + (r >> 2) * 8 + (r & 3);
-          if (jj < j_lo || jj > j_hi) s[kb][r] = kNegInf;
+          const uint32_t x = (uint32_t)(base + kb * 32 + (r >> 2) * 8 + (r & 3));
+          if (x >= cnt) s[kb][r] = kNegInf;
         }
     }
     float mx = kNegInf;
