@@ -95,6 +95,15 @@ void fill_opts(fa::PrefillParams& p, const fa_attn_opts* o, float scale) {
   p.wr = window_side(o, false);
 }
 
+// Keys a query row can see besides its own position: the left window side plus
+// the right one (0 under causal), or -1 when either side is unbounded.
+int key_span(const fa_attn_opts* o) {
+  const int wl = window_side(o, true), wr = window_side(o, false);
+  const bool causal = o && o->causal;
+  if (wl < 0 || (!causal && wr < 0)) return -1;
+  return (int)std::min<int64_t>((int64_t)wl + (causal ? 0 : wr), 1 << 30);
+}
+
 fa_status launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -221,7 +230,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, const void* k, const void* v, vo
   if ((st = check_strides("q", qs, 3)) || (st = check_strides("k", ks, 3)) || (st = check_strides("v", vs, 3)) ||
       (st = check_strides("out", os, 3)))
     return st;
-  const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, Sq, device_cus());
+  const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, Sq, device_cus(), key_span(opts));
   const int64_t nqt = (Sq + bm - 1) / bm;
   if (!dispatch_fits(nqt * Hq * (int64_t)B, 512)) return grid_too_large(nqt * Hq * (int64_t)B, 512);
 
@@ -319,7 +328,7 @@ fa_status fa_fwd_varlen(fa_dtype dtype, const void* q, const void* k, const void
   if ((st = check_strides("q", qs, 2)) || (st = check_strides("k", ks, 2)) || (st = check_strides("v", vs, 2)) ||
       (st = check_strides("out", os, 2)))
     return st;
-  const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, max_seqlen_q, device_cus());
+  const int bm = fa::prefill_block_m(D, (int64_t)B * Hq, max_seqlen_q, device_cus(), key_span(opts));
   const int64_t nqt = (max_seqlen_q + bm - 1) / bm;
   if (!dispatch_fits(nqt * Hq * (int64_t)B, 512)) return grid_too_large(nqt * Hq * (int64_t)B, 512);
   if (debug_checks() && (st = debug_check_cu(cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, max_seqlen_k, total_q,

@@ -166,7 +166,9 @@ int backward_block_m(int D);   // queries per dQ workgroup
 // query rows per prefill workgroup for head dim D (the host sizes the grid with it)
 // query rows per prefill workgroup for B*Hq = heads and the longest query
 // sequence, on a device with cus compute units
-int prefill_block_m(int D, int64_t heads, int max_sq, int cus);
+// span: keys a row can see besides its own position (window sides, right side 0
+// when causal), or -1 when unbounded
+int prefill_block_m(int D, int64_t heads, int max_sq, int cus, int span);
 
 // Heads per longest-first group for a grid of n_units heads x n_tiles tiles of
 // unequal length: enough tiles per group to fill the about 64 workgroups an

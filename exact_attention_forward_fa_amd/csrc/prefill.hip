@@ -71,7 +71,7 @@ template <int D> constexpr int k_stride() { return D + 8; }
 template <int D> constexpr int v_stride() { return D + (D == 96 ? 0 : D == 32 ? 64 : FA_PREFILL_VPAD); }
 
 template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI, bool F8 = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 || (NW <= 2 && D >= 96) ? 1 : D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? 4 : FA_PREFILL_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 || (NW <= 2 && D >= 96) ? 1 : D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? (D == 64 && NW == 4 ? 3 : 4) : FA_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -946,11 +946,17 @@ template <> struct Shape<128> { static constexpr int NW = FA_PREFILL_NW128, RB =
 // when B*Hq*ceil(Sq/256) workgroups would fill fewer than two per CU it drops
 // to 4 waves (128 rows) or 2 waves (64 rows), so more CUs get work (each wave
 // still owns 32 rows; the workgroups share K/V tiles among fewer waves).
-template <int D> static int block_m_of(int64_t heads, int max_sq, int cus) {
+template <int D> static int block_m_of(int64_t heads, int max_sq, int cus, int span) {
   using S = Shape<D>;
   if (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128)) return 8 * 32;
   if (S::NW != 8 || S::RB != 1) return S::NW * 32 * S::RB;
   auto wgs = [&](int bm) { return heads * ((max_sq + bm - 1) / bm); };
+  // D = 64 under a narrow window (a row sees at most 512 keys besides its own):
+  // a 256-row workgroup walks 256 + span keys of which each wave needs 32 +
+  // span, so 128-row workgroups (3 per CU, 3 waves per SIMD) waste fewer
+  // barrier steps: B=4, S=4096, H=32 window (256,0) 336 -> 366 TFLOP/s,
+  // (256,256) 530 -> 540
+  if (D == 64 && span >= 0 && span <= 512 && wgs(128) >= (int64_t)cus) return 128;
   // D = 96: 4-wave workgroups measured faster even on full grids (656 against
   // 615 TFLOP/s at B=4, S=4096, H=32 causal), 8 waves splitting its 12-piece
   // rows less evenly
@@ -959,13 +965,13 @@ template <int D> static int block_m_of(int64_t heads, int max_sq, int cus) {
   return 64;
 }
 
-int prefill_block_m(int D, int64_t heads, int max_sq, int cus) {
+int prefill_block_m(int D, int64_t heads, int max_sq, int cus, int span) {
   switch (D) {
-    case 32: return block_m_of<32>(heads, max_sq, cus);
-    case 64: return block_m_of<64>(heads, max_sq, cus);
-    case 96: return block_m_of<96>(heads, max_sq, cus);
-    case 256: return block_m_of<256>(heads, max_sq, cus);
-    default: return block_m_of<128>(heads, max_sq, cus);
+    case 32: return block_m_of<32>(heads, max_sq, cus, span);
+    case 64: return block_m_of<64>(heads, max_sq, cus, span);
+    case 96: return block_m_of<96>(heads, max_sq, cus, span);
+    case 256: return block_m_of<256>(heads, max_sq, cus, span);
+    default: return block_m_of<128>(heads, max_sq, cus, span);
   }
 }
 
