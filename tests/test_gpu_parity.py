@@ -677,9 +677,11 @@ def test_fp8_prefill_full_size_all_rows():
     check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, "fp8 c3_causal")
 
 
-@pytest.mark.parametrize("opts", [dict(causal=True), dict(window=(100, 20)), dict(causal=True, softcap=8.0)])
+@pytest.mark.parametrize("opts", [dict(causal=True), dict(window=(100, 20)), dict(window=(600, 20)),
+                                  dict(causal=True, softcap=8.0)])
 def test_prefill_same_bits_for_any_workgroup_rows(opts):
-    """A small grid runs 64-row workgroups and a large one 256-row workgroups; each
+    """A small grid runs 64-row workgroups and a large one 256-row workgroups
+    (128 rows under a window of at most 512 keys besides the row's own); each
     wave owns the same 32 rows and walks the same tiles either way, so the
     results of one (batch, head) agree bit for bit."""
     q, k, v = inputs.dense_qkv(1, 512, 600, 2, 2, 64, torch.float16, seed=4711)
