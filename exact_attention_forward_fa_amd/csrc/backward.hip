@@ -31,6 +31,7 @@
 // Both streaming kernels hold their LDS tiles in an XOR-swizzled row-major
 // layout (swz below) that serves the plain 16-byte operand reads and the
 // transposing reads without bank conflicts.
+#include <algorithm>
 #include <type_traits>
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
@@ -64,25 +65,41 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
   using V8 = typename E::V8;
   constexpr int CH = D / 8;                                  // 16-byte pieces per row
   constexpr int CHP = CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32;   // lanes per row (power of two)
-  constexpr int RPB = 256 / CHP;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CHP;   // (b, i, h), h fastest
+  constexpr int RPB = 256 / CHP;                             // rows per pass of the workgroup
+  constexpr int RPT = 4;                                     // passes, their loads issued together
+  // a workgroup takes RPB * RPT consecutive positions i of one (b, h): no
+  // per-row index division, and its delta stores fill whole cache lines
   const int c = threadIdx.x % CHP;
-  const int64_t nrows = (int64_t)p.delta_B * p.delta_S * p.Hq;
-  float acc = 0.f;
-  int64_t b = 0, i = 0, h = 0;
-  if (row < nrows && c < CH) {
-    h = row % p.Hq;
-    const int64_t bi = row / p.Hq;
-    i = bi % p.delta_S;
-    b = bi / p.delta_S;
-    const V8 x = *(const V8*)((const T*)p.out + b * p.o_sb + i * p.o_ss + h * p.o_sh + c * 8);
-    const V8 y = *(const V8*)((const T*)p.dout + b * p.do_sb + i * p.do_ss + h * p.do_sh + c * 8);
+  const int i0 = blockIdx.x * (RPB * RPT) + threadIdx.x / CHP;
+  const int64_t BH = (int64_t)p.delta_B * p.Hq;
+  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    const int64_t b = bh / p.Hq, h = bh - b * p.Hq;
+    const T* ob = (const T*)p.out + b * p.o_sb + h * p.o_sh + c * 8;
+    const T* db = (const T*)p.dout + b * p.do_sb + h * p.do_sh + c * 8;
+    float* dl = p.delta + b * p.dl_sb + h * p.dl_sh;
+    V8 x[RPT], y[RPT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+    for (int k = 0; k < RPT; ++k) {
+      const int i = i0 + k * RPB;
+      if (i < p.delta_S && c < CH) {
+        x[k] = *(const V8*)(ob + (int64_t)i * p.o_ss);
+        y[k] = *(const V8*)(db + (int64_t)i * p.do_ss);
+      } else {
+        x[k] = V8{};
+        y[k] = V8{};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[k][e], (float)y[k][e], acc);
+#pragma unroll
+      for (int m = CHP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+      const int i = i0 + k * RPB;
+      if (i < p.delta_S && c == 0) dl[i] = acc;
+    }
   }
-#pragma unroll
-  for (int m = CHP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < nrows && c == 0) p.delta[b * p.dl_sb + h * p.dl_sh + i] = acc;
 }
 
 // Score of one (query, key) pair in log2 units from the raw product x = q·k, and
@@ -707,10 +724,11 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
 template <class E, int D>
 hipError_t launch_bwd_d(const BackwardParams& p, hipStream_t s) {
   constexpr int CH = D / 8;
-  constexpr int RPB = 256 / (CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32);
-  const int64_t rows = (int64_t)p.delta_B * p.delta_S * p.Hq;
-  if (rows > 0) {
-    hipLaunchKernelGGL((bwd_delta_kernel<E, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  constexpr int RPW = 4 * 256 / (CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32);   // positions per workgroup
+  const int64_t bh = (int64_t)p.delta_B * p.Hq;
+  if (bh > 0 && p.delta_S > 0) {
+    const dim3 grid((unsigned)((p.delta_S + RPW - 1) / RPW), (unsigned)std::min<int64_t>(bh, 65535));
+    hipLaunchKernelGGL((bwd_delta_kernel<E, D>), grid, dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
