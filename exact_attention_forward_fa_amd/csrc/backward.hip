@@ -14,8 +14,7 @@
 //   dU = dS (1 - t²) under softcap (t = tanh of the capped argument), else dS,
 //   dQ_i += scale dU K_j,  dK_j += scale dU Q_i.
 //
-// Three kernels:
-//  * bwd_delta_kernel: delta_i = dO_i · O_i (fp32), one row per D/8 lanes.
+// Two kernels, the dQ kernel first:
 //  * bwd_dkdv_kernel: one workgroup per (key tile, kv head, batch); each wave
 //    owns 32 keys, keeps their K and V rows in registers and their dK and dV
 //    accumulators in registers, and streams the query tiles of every query head
@@ -27,11 +26,11 @@
 //    owns 32 queries, keeps their Q and dO rows in registers, and streams K and V
 //    tiles through LDS.  Sᵀ = K Qᵀ and dPᵀ = V dOᵀ put the query on the lane
 //    side, so dS is in the A-operand layout of dQ += dS K, with K read
-//    transposed.
+//    transposed.  It also forms delta_i from the dO row it holds and the O row,
+//    and stores it in the workspace for the dK/dV kernel.
 // Both streaming kernels hold their LDS tiles in an XOR-swizzled row-major
 // layout (swz below) that serves the plain 16-byte operand reads and the
 // transposing reads without bank conflicts.
-#include <algorithm>
 #include <type_traits>
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
@@ -54,52 +53,6 @@ __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (D >= 128) return r * D + 8 * (c ^ (4 * (r & 3) + ((r >> 2) & 3)));
   else if constexpr (D == 64) return r * D + 8 * (c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3)));
   else return r * D + 8 * (c ^ ((r >> 2) & 3));
-}
-
-// ---------------------------------------------------------------------------
-// delta_i = sum_d dO[i, d] * O[i, d]
-// ---------------------------------------------------------------------------
-template <class E, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BackwardParams p) {
-  using T = typename E::T;
-  using V8 = typename E::V8;
-  constexpr int CH = D / 8;                                  // 16-byte pieces per row
-  constexpr int CHP = CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32;   // lanes per row (power of two)
-  constexpr int RPB = 256 / CHP;                             // rows per pass of the workgroup
-  constexpr int RPT = 4;                                     // passes, their loads issued together
-  // a workgroup takes RPB * RPT consecutive positions i of one (b, h): no
-  // per-row index division, and its delta stores fill whole cache lines
-  const int c = threadIdx.x % CHP;
-  const int i0 = blockIdx.x * (RPB * RPT) + threadIdx.x / CHP;
-  const int64_t BH = (int64_t)p.delta_B * p.Hq;
-  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
-    const int64_t b = bh / p.Hq, h = bh - b * p.Hq;
-    const T* ob = (const T*)p.out + b * p.o_sb + h * p.o_sh + c * 8;
-    const T* db = (const T*)p.dout + b * p.do_sb + h * p.do_sh + c * 8;
-    float* dl = p.delta + b * p.dl_sb + h * p.dl_sh;
-    V8 x[RPT], y[RPT];
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      const int i = i0 + k * RPB;
-      if (i < p.delta_S && c < CH) {
-        x[k] = *(const V8*)(ob + (int64_t)i * p.o_ss);
-        y[k] = *(const V8*)(db + (int64_t)i * p.do_ss);
-      } else {
-        x[k] = V8{};
-        y[k] = V8{};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[k][e], (float)y[k][e], acc);
-#pragma unroll
-      for (int m = CHP / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-      const int i = i0 + k * RPB;
-      if (i < p.delta_S && c == 0) dl[i] = acc;
-    }
-  }
 }
 
 // Score of one (query, key) pair in log2 units from the raw product x = q·k, and
@@ -515,19 +468,32 @@ void bwd_dq_kernel(BackwardParams p) {
   // Q and dO rows of the lane's query: B operands of Sᵀ = K Qᵀ and dPᵀ = V dOᵀ
   V8 qr[DC], gr[G_LDS ? 1 : DC];
   T* const gw = gsm + (G_LDS ? wave * 32 * D : 0);   // the wave's dO rows (G_LDS)
+  // delta_i = dO_i · O_i of the lane's row: each lane holds half of the row's dO
+  // and reads the same half of O, and the halves meet across lane ^ 32.  The
+  // lane with hi = 0 also stores it for the dK/dV kernel, which runs after
+  // this one.
+  float Dl;
   {
     const T* qp = (const T*)p.q + bq * p.q_sb + (int64_t)(qbase + ic) * p.q_ss + (int64_t)hq * p.q_sh + hi * 8;
     const T* gp = (const T*)p.dout + bq * p.do_sb + (int64_t)(qbase + ic) * p.do_ss + (int64_t)hq * p.do_sh + hi * 8;
+    const T* op = (const T*)p.out + bq * p.o_sb + (int64_t)(qbase + ic) * p.o_ss + (int64_t)hq * p.o_sh + hi * 8;
+    float acc = 0.f;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       qr[dc] = *(const V8*)(qp + dc * 16);
-      if constexpr (G_LDS) *(V8*)(gw + swz<D>(l32, 2 * dc + hi)) = *(const V8*)(gp + dc * 16);
-      else gr[dc] = *(const V8*)(gp + dc * 16);
+      const V8 g = *(const V8*)(gp + dc * 16);
+      const V8 o = *(const V8*)(op + dc * 16);
+      if constexpr (G_LDS) *(V8*)(gw + swz<D>(l32, 2 * dc + hi)) = g;
+      else gr[dc] = g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
     }
+    acc += __shfl_xor(acc, 32);
+    Dl = row_ok ? acc : 0.f;
+    if (row_ok && hi == 0) p.delta[bq * p.dl_sb + (int64_t)hq * p.dl_sh + qbase + ic] = acc;
   }
   const float lse = p.lse[bq * p.lse_sb + (int64_t)hq * p.lse_sh + qbase + ic];
   const float L = (row_ok && lse != kNegInf) ? lse * kLog2e : __builtin_inff();
-  const float Dl = row_ok ? p.delta[bq * p.dl_sb + (int64_t)hq * p.dl_sh + qbase + ic] : 0.f;
   const float sl2 = p.scale * kLog2e;
   const float cap_l2 = p.softcap * kLog2e;
   const float cap_in = 2.f * p.scale * kLog2e / (SOFTCAP ? p.softcap : 1.f);
@@ -692,6 +658,18 @@ int backward_block_m(int D) { return (D >= 256 ? 4 : D >= 128 ? FA_BWD_Q_NW128 :
 
 template <class E, int D, bool SOFTCAP, bool ALIBI>
 hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
+  // dQ first: it also computes delta = rowsum(dO * O) for its rows and stores it
+  // in the workspace, where the dK/dV kernel reads it
+  const int64_t gq = (int64_t)p.n_qtiles * p.B * p.Hq;
+  if (gq > 0) {
+    BackwardParams pq = p;
+    pq.remap_xcd = ((int64_t)p.B * p.Hq) % 8 == 0;
+    pq.order_group = order_group(p.causal != 0, (int64_t)p.B * p.Hq, p.n_qtiles, pq.remap_xcd);
+    constexpr int NWQ = bwd_dq_waves<D>();
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, NWQ, SOFTCAP, ALIBI>), dim3((unsigned)gq), dim3(NWQ * 64), 0, s, pq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   constexpr int NWK = bwd_dkdv_waves<D>();
   const int64_t gk = (int64_t)p.n_ktiles * p.B * p.Hkv;
   if (gk > 0) {
@@ -706,16 +684,6 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
     } else {
       hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NWK, SOFTCAP, ALIBI, 0>), dim3((unsigned)gk), dim3(NWK * 64), 0, s, pk);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t gq = (int64_t)p.n_qtiles * p.B * p.Hq;
-  if (gq > 0) {
-    BackwardParams pq = p;
-    pq.remap_xcd = ((int64_t)p.B * p.Hq) % 8 == 0;
-    pq.order_group = order_group(p.causal != 0, (int64_t)p.B * p.Hq, p.n_qtiles, pq.remap_xcd);
-    constexpr int NWQ = bwd_dq_waves<D>();
-    hipLaunchKernelGGL((bwd_dq_kernel<E, D, NWQ, SOFTCAP, ALIBI>), dim3((unsigned)gq), dim3(NWQ * 64), 0, s, pq);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -723,15 +691,6 @@ hipError_t launch_bwd_main(const BackwardParams& p, hipStream_t s) {
 
 template <class E, int D>
 hipError_t launch_bwd_d(const BackwardParams& p, hipStream_t s) {
-  constexpr int CH = D / 8;
-  constexpr int RPW = 4 * 256 / (CH <= 4 ? 4 : CH <= 8 ? 8 : CH <= 16 ? 16 : 32);   // positions per workgroup
-  const int64_t bh = (int64_t)p.delta_B * p.Hq;
-  if (bh > 0 && p.delta_S > 0) {
-    const dim3 grid((unsigned)((p.delta_S + RPW - 1) / RPW), (unsigned)std::min<int64_t>(bh, 65535));
-    hipLaunchKernelGGL((bwd_delta_kernel<E, D>), grid, dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const bool cap = p.softcap > 0.f, al = p.alibi != nullptr;
   if (cap && al) return launch_bwd_main<E, D, true, true>(p, s);
   if (cap) return launch_bwd_main<E, D, true, false>(p, s);

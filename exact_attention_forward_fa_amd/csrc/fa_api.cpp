@@ -674,7 +674,6 @@ fa_status fa_bwd(fa_dtype dtype, const void* dout, const void* q, const void* k,
   p.dl_sb = (int64_t)Hq * Sq; p.dl_sh = Sq;
   p.cu_seqlens_q = nullptr; p.cu_seqlens_k = nullptr;
   p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
-  p.delta_B = B; p.delta_S = Sq;
   p.scale = scale;
   p.softcap = opts ? opts->softcap : 0.f;
   p.alibi = opts ? opts->alibi_slopes : nullptr;
@@ -748,7 +747,6 @@ fa_status fa_bwd_varlen(fa_dtype dtype, const void* dout, const void* q, const v
   p.dl_sb = 0; p.dl_sh = total_q;
   p.cu_seqlens_q = cu_seqlens_q; p.cu_seqlens_k = cu_seqlens_k;
   p.B = B; p.Sq = max_seqlen_q; p.Sk = max_seqlen_k; p.Hq = Hq; p.Hkv = Hkv; p.group = Hq / Hkv;
-  p.delta_B = 1; p.delta_S = total_q;
   p.scale = scale;
   p.softcap = opts ? opts->softcap : 0.f;
   p.alibi = opts ? opts->alibi_slopes : nullptr;

@@ -126,7 +126,6 @@ struct BackwardParams {
   int64_t lse_sb, lse_sh;      // as for the forward: element (b, h, i) at b*lse_sb + h*lse_sh + row_base + i
   int64_t dl_sb, dl_sh;
   int B, Sq, Sk, Hq, Hkv, group;   // varlen: Sq/Sk hold max_seqlen_q/k
-  int delta_B, delta_S;        // rows of the delta kernel: (delta_B, delta_S, Hq); varlen (1, total_q)
   float scale;
   float softcap;
   const float* alibi;
