@@ -79,12 +79,15 @@ void prefill_kernel(PrefillParams p) {
   // F8: q, k, v are fp8 e4m3 (OCP); Q K^T runs on the fp8 MFMA, V is widened
   // exactly to bf16 (T) on its way into LDS, and P V, out and lse are as for bf16
   using TI = std::conditional_t<F8, uint8_t, T>;          // element type of q, k, v
-  using QV = std::conditional_t<F8, long, V8>;            // 8-element operand of Q K^T
+  // operand of Q K^T: 8 elements (v_mfma_f32_32x32x16_{f16,bf16}) or, for fp8,
+  // 32 (v_mfma_f32_32x32x64_f8f6f4: one instruction per 64 of the D products)
+  using QV = std::conditional_t<F8, i32x8, V8>;
   using KST = std::conditional_t<F8, u32x2, u32x4>;       // 8 staged elements of K or V
   constexpr int BM = NW * 32 * RB;        // query rows per workgroup
   constexpr int CH = D / 8;               // 16-byte chunks per row
   constexpr int KB = BN / 32;             // 32-key blocks per tile
-  constexpr int DC = D / 16;              // contraction steps of Q K^T
+  constexpr int DC = F8 ? D / 64 : D / 16;   // contraction steps of Q K^T
+  constexpr int DW = F8 ? 64 : 16;        // elements of d per step
   constexpr int DB = D / 32;              // 32-wide blocks of the output
   constexpr int NT = NW * 64;
   constexpr int LOADS = (BN * CH + NT - 1) / NT;   // 16-byte loads per thread per tile, for K and for V
@@ -95,9 +98,9 @@ void prefill_kernel(PrefillParams p) {
   constexpr bool PLAIN = !SOFTCAP && !ALIBI;
 
   constexpr int KS = k_stride<D>(), VS = v_stride<D>();
-  // K row stride in elements of TI: fp8 rows of D+8 bytes keep the 8-byte operand
-  // reads of 16 lanes on distinct banks
-  constexpr int KSI = F8 ? D + 8 : KS;
+  // K row stride in elements of TI: fp8 rows of D+16 bytes keep the 16-byte
+  // pieces of the 32-byte operand reads aligned, and 16 lanes on distinct banks
+  constexpr int KSI = F8 ? D + 16 : KS;
   __shared__ __attribute__((aligned(16))) T ksm[2][BN * KS];   // K tiles, double-buffered
   __shared__ __attribute__((aligned(16))) T vsm[2][BN * VS];   // V tiles
 
@@ -168,14 +171,25 @@ void prefill_kernel(PrefillParams p) {
     if (lo_min[rb] > hi_max[rb]) blk_live[rb] = false;   // no row of the block sees any key
   }
 
-  // ---- Q operand (B of S^T = K Q^T): lane holds row qrow, d = 16*dc + 8*hi .. +7
+  // ---- Q operand (B of S^T = K Q^T): lane holds row qrow, d = DW*dc + (DW/2)*hi
+  // .. +DW/2-1 (fp8 rows are only 8-byte aligned: read in 8-byte pieces)
   QV qr[RB][DC];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      if (row_ok[rb]) qr[rb][dc] = *(const QV*)(qp + (int64_t)qrow[rb] * p.q_ss + dc * 16 + hi * 8);
-      else qr[rb][dc] = QV{};
+      const TI* qrp = qp + (int64_t)qrow[rb] * p.q_ss + dc * DW + hi * (DW / 2);
+      if (!row_ok[rb]) {
+        qr[rb][dc] = QV{};
+      } else if constexpr (F8) {
+        u32x2 w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = *(const u32x2*)(qrp + 8 * u);
+        qr[rb][dc] = i32x8{(int)w[0][0], (int)w[0][1], (int)w[1][0], (int)w[1][1],
+                           (int)w[2][0], (int)w[2][1], (int)w[3][0], (int)w[3][1]};
+      } else {
+        qr[rb][dc] = *(const QV*)qrp;
+      }
     }
 
   float slope_l2 = 0.f, ipf[RB];
@@ -266,15 +280,23 @@ void prefill_kernel(PrefillParams p) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[rb][kb] = f32x16{};
-    const TI* kbase = reinterpret_cast<const TI*>(Ks) + l32 * KSI + hi * 8;
+    const TI* kbase = reinterpret_cast<const TI*>(Ks) + l32 * KSI + hi * (DW / 2);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const QV a = *(const QV*)(kbase + kb * 32 * KSI + dc * 16);
+        QV a;
+        if constexpr (F8) {
+          const u32x4 a0 = *(const u32x4*)(kbase + kb * 32 * KSI + dc * DW);
+          const u32x4 a1 = *(const u32x4*)(kbase + kb * 32 * KSI + dc * DW + 16);
+          a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        } else {
+          a = *(const QV*)(kbase + kb * 32 * KSI + dc * DW);
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          if constexpr (F8) s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, qr[rb][dc], s[rb][kb], 0, 0, 0);
+          // fp8 e4m3 (format 0) for both operands, no block scales
+          if constexpr (F8) s[rb][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qr[rb][dc], s[rb][kb], 0, 0, 0, 0, 0, 0);
           else s[rb][kb] = E::mfma32(a, qr[rb][dc], s[rb][kb]);
         }
       }
