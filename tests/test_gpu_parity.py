@@ -663,6 +663,28 @@ def test_fp8_prefill(case):
     check(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"fp8 {case}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_rows_8_byte_aligned_equal_contiguous(D):
+    """fp8 q, k and v whose rows start only 8 bytes apart from a 16-byte boundary
+    (head stride D + 8 bytes): the 32-byte Q operands are read in 8-byte pieces
+    and K is staged 8 bytes at a time, so the bits equal those of contiguous
+    copies."""
+    print("case fp8 8-byte rows", D, flush=True)
+    q, k, v = inputs.dense_qkv(2, 140, 200, 4, 2, D, torch.float32, seed=1750 + D)
+    q8, k8, v8 = (t.to(torch.float8_e4m3fn) for t in (q, k, v))
+
+    def padded(t):
+        B, S, H, _ = t.shape
+        store = torch.zeros(B, S, H, D + 8, dtype=torch.uint8)
+        store[..., :D] = t.view(torch.uint8)
+        return store.to(DEV).view(torch.float8_e4m3fn)[..., :D]
+
+    a = fa.fwd(padded(q8), padded(k8), padded(v8), causal=True)
+    b = fa.fwd(q8.to(DEV), k8.to(DEV), v8.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].cpu(), b[0].cpu()) and torch.equal(a[1].cpu(), b[1].cpu())
+
+
 def test_fp8_prefill_full_size_all_rows():
     """The fp8 prefill at the size and in the launch configuration the benchmark
     times (B=4, S=4096, H=32, D=64 causal, the fp16 inputs converted to e4m3,
@@ -678,7 +700,7 @@ def test_fp8_prefill_full_size_all_rows():
 
 
 @pytest.mark.parametrize("opts", [dict(causal=True), dict(window=(100, 20)), dict(window=(600, 20)),
-                                  dict(causal=True, softcap=8.0)])
+                                  dict(causal=True, softcap=8.0), dict(causal=True, window=(100, 0), softcap=8.0)])
 def test_prefill_same_bits_for_any_workgroup_rows(opts):
     """A small grid runs 64-row workgroups and a large one 256-row workgroups
     (128 rows under a window of at most 512 keys besides the row's own); each
