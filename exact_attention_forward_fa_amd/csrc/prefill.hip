@@ -70,6 +70,11 @@ template <int D> constexpr int k_stride() { return D + 8; }
 #endif
 template <int D> constexpr int v_stride() { return D + (D == 96 ? 0 : D == 32 ? 64 : FA_PREFILL_VPAD); }
 
+// Register budgets (waves per SIMD): four for the plain kernels up to D = 64,
+// except three for the 4-wave D = 64 instance (its two 16-byte K/V loads per
+// thread and tile need about 155 registers; it runs the narrow windows, three
+// workgroups per CU); one at D = 256 and for the 2-wave D >= 96 instances;
+// FA_PREFILL_WAVES_PER_EU otherwise.
 template <class E, int D, int BN, int NW, int RB, bool SOFTCAP, bool ALIBI, bool F8 = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 || (NW <= 2 && D >= 96) ? 1 : D <= 64 && RB == 1 && !SOFTCAP && !ALIBI ? (D == 64 && NW == 4 ? 3 : 4) : FA_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p) {
