@@ -46,10 +46,15 @@ constexpr float kPreciseOut = 1.f;
 template <class E> constexpr float precise_out_pp() { return std::is_same_v<E, BF16> ? 2.f : 1.f; }
 
 // Head dims from which the ping-pong kernel is used.  With D = 64 the softmax
-// phase outweighs the MFMA phase and a single wave per SIMD cannot issue VALU
-// work fast enough, so the 4-waves-per-SIMD kernel is faster there.
+// phase outweighs the MFMA phase: the ping-pong kernel there, even with the
+// lean softmax phase, runs at the main kernel's rate and not above it.
 #ifndef FA_PREFILL_PINGPONG_MIN_D
 #define FA_PREFILL_PINGPONG_MIN_D 128
+#endif
+// 1: the ping-pong kernel's lean softmax phase (lazy max, fp32 sum only) for
+// plain masks; softcap and ALiBi keep the full phase (see prefill_pp_kernel)
+#ifndef FA_PP_LEAN
+#define FA_PP_LEAN 1
 #endif
 #ifndef FA_PREFILL_WAVES_PER_EU
 #define FA_PREFILL_WAVES_PER_EU 2    // register budget: 256 VGPRs+AGPRs per wave
@@ -605,8 +610,14 @@ void prefill_kernel(PrefillParams p) {
 // exponentials.  Phases end at workgroup barriers; K/V tiles rotate through
 // three LDS stages, each wave staging its share of tile j+1 during GEMM phase
 // j-1 and storing it during GEMM phase j.
+// LEAN selects the softmax phase of prefill_kernel (P against the running max
+// without a max reduction, the fp32 sum of P normalising out); otherwise the
+// max is taken on every tile and out is normalised by the sum of the rounded
+// P, which suits softcap and ALiBi: steep ALiBi slopes raise the max within
+// most tiles, and the rounded-P normalisation lets bf16 rows up to |out| = 2
+// skip the precise pass.
 // ---------------------------------------------------------------------------
-template <class E, int D, int BN, bool SOFTCAP, bool ALIBI>
+template <class E, int D, int BN, bool SOFTCAP, bool ALIBI, bool LEAN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(FA_PREFILL_WAVES_PER_EU)))
 void prefill_pp_kernel(PrefillParams p) {
   using T = typename E::T;
@@ -727,7 +738,8 @@ void prefill_pp_kernel(PrefillParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   // running row max m (log2 units), sum l of the rounded P that feeds P V (it
-  // normalises out) and sum lx of the fp32 P (it gives lse)
+  // normalises out; not kept by the lean phase, which normalises by lx) and sum
+  // lx of the fp32 P (it gives lse)
   float m = kNegInf, l = 0.f, lx = 0.f;
   f32x16 s[KB];
   V2 pk[KB][8];
@@ -750,6 +762,7 @@ void prefill_pp_kernel(PrefillParams p) {
     __builtin_amdgcn_s_setprio(1);
     if (j >= 1 && j + 1 < n_t) swrite(st_w);
     if (j >= 1 && j + 2 < n_t) gload(j + 2);
+    {
     if (j < n_t) {
       const T* kb_ = ksm[st_q] + l32 * KS + hi * 8;
 #pragma unroll
@@ -785,6 +798,7 @@ void prefill_pp_kernel(PrefillParams p) {
           o[db] = E::mfma32(a, bop, o[db]);
         }
       }
+    }
     }
     __builtin_amdgcn_s_setprio(0);
     barrier();
@@ -824,6 +838,59 @@ void prefill_pp_kernel(PrefillParams p) {
           if (x >= cnt) s[kb][r] = kNegInf;
         }
     }
+    if constexpr (LEAN) {
+      // P against the running max m without a max reduction, kept when no
+      // lane's sum of the tile's P exceeds 2^kTau; otherwise (a row without a
+      // max yet, or scores well above m) m moves to the exact new max, O and lx
+      // are rescaled and P is formed again from the scores still in registers.
+      float lxs = 0.f;
+      bool redo = __any(m == kNegInf);
+      if (!redo) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = exp2_fast(fmaf(s[kb][r], mult, -m));
+            const float p1 = exp2_fast(fmaf(s[kb][r + 1], mult, -m));
+            pk[kb][r >> 1] = E::pack(p0, p1);
+            lxs += p0 + p1;
+          }
+        redo = __any(lxs > kTauPow);
+      }
+      if (redo) {
+        float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 4) {
+            mx0 = fmaxf(fmaxf(mx0, s[kb][r]), s[kb][r + 1]);
+            mx1 = fmaxf(fmaxf(mx1, s[kb][r + 2]), s[kb][r + 3]);
+          }
+        const float m_new = fmaxf(m, max_halves(fmaxf(mx0, mx1)) * mult);
+        if (__any(m_new > m)) {
+          const float alpha = m_new == kNegInf ? 1.f : exp2_fast(m - m_new);
+          m = m_new;
+          lx *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
+        const float m_use = m == kNegInf ? 0.f : m;
+        lxs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = exp2_fast(fmaf(s[kb][r], mult, -m_use));
+            const float p1 = exp2_fast(fmaf(s[kb][r + 1], mult, -m_use));
+            pk[kb][r >> 1] = E::pack(p0, p1);
+            lxs += p0 + p1;
+          }
+      }
+      lx += lxs;
+      barrier();
+      st_q = st_w;
+      continue;
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -858,7 +925,7 @@ void prefill_pp_kernel(PrefillParams p) {
   }
   if (grp == 0) barrier();                 // matches group 1's initial offset
 
-  // out = O / norm (l, or lx after the precise pass, whose O is the product with
+  // out = O / norm (l; lx in the lean phase and after the precise pass, whose O is the product with
   // P itself), lse = (m + log2 lx) * ln 2
   auto write_row = [&](float norm) __attribute__((always_inline)) {
     const float lt = sum_halves(norm);
@@ -890,10 +957,11 @@ void prefill_pp_kernel(PrefillParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) om = fmaxf(om, fabsf(o[db][r]));
-    need = row_ok && lt > 0.f && om / lt >= precise_out_pp<E>();
+    const float lnorm = LEAN ? sum_halves(lx) : lt;
+    need = row_ok && lnorm > 0.f && om / lnorm >= (LEAN ? kPreciseOut : precise_out_pp<E>());
   }
   const bool wave_need = __any(need);
-  if (!wave_need) write_row(l);
+  if (!wave_need) write_row(LEAN ? lx : l);
   if (__syncthreads_or(wave_need)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x16{};
@@ -1013,7 +1081,7 @@ template <class E, int D, bool SC, bool AL>
 static hipError_t launch_one(const PrefillParams& p, hipStream_t s) {
   using S = Shape<D>;
   if constexpr (D >= FA_PREFILL_PINGPONG_MIN_D && (D == 64 || D == 128)) {
-    launch_k<prefill_pp_kernel<E, D, 64, SC, AL>>(512, p, s);
+    launch_k<prefill_pp_kernel<E, D, 64, SC, AL, FA_PP_LEAN && !SC && !AL>>(512, p, s);
   } else if constexpr (S::NW == 8 && S::RB == 1) {
     // fewer rows per workgroup when the grid would leave CUs idle (see prefill_block_m)
     if (p.block_m == 64)
