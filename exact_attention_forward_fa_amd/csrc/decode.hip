@@ -27,7 +27,10 @@
 //    the K/V loads of the chunk in between: vector-memory results return in
 //    order, so waiting for the page numbers never waits for K/V data in flight;
 //  * an item's token range is clamped to the union of its rows' sliding windows,
-//    so keys no row can see are never read.
+//    so keys no row can see are never read;
+//  * at D = 128 on a paged cache under 4 GiB (the KD form), K goes from HBM
+//    straight into MFMA operand registers and only V is staged in LDS, in two
+//    tiles, so K of two chunks can be in flight while one is computed.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -100,7 +103,7 @@ struct DecodeChunk {
 // most two pages), 2 = paged with smaller pages.  OFF32: the cache holds fewer
 // than 2^32 bytes, so byte offsets into it fit in 32 bits.
 // ---------------------------------------------------------------------------
-template <class E, int D, int MODE, bool OFF32>
+template <class E, int D, int MODE, bool OFF32, bool KD>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WPE))) void decode_kernel(DecodeParams p) {
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -119,8 +122,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   constexpr int NE = MODE == 2 ? NL : 1;  // page numbers a lane holds per chunk
   static_assert(NL * 64 == C * CHP, "");
   constexpr int NG = C / 16;              // 16-token groups per chunk (MFMA M blocks of S^T)
-  __shared__ __attribute__((aligned(16))) T vbuf[C * VROW];
-  __shared__ __attribute__((aligned(16))) T kbuf[C * KROW];
+  // KD: K goes from HBM straight into MFMA operand registers and only V is
+  // staged in LDS, in two tiles (see the KD pipeline at the end)
+  __shared__ __attribute__((aligned(16))) T vbuf[(KD ? 2 : 1) * C * VROW];
+  __shared__ __attribute__((aligned(16))) T kbuf[KD ? 8 : C * KROW];
 
   const int lane = threadIdx.x, n = lane & 15, q4 = lane >> 4;
   lds_poison(vbuf, sizeof(vbuf), lane, 64);
@@ -390,7 +395,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     for (int db = 0; db < DBK; ++db) o[db] = f32x4{};
   };
 
-  auto compute = [&](const DecodeChunk& d) __attribute__((always_inline)) {
+  // kk: with KD, the chunk's K operands in registers (K[token 16g + n][d = 32ks +
+  // 8q4 ..] in kk[g * KSTEP + ks]); vt: the LDS tile holding the chunk's V rows
+  // after_scores runs once S^T has been formed (the KD pipeline loads the next
+  // K operands into kk there)
+  auto compute = [&](const DecodeChunk& d, const u32x4* kk, const T* vt, auto&& after_scores)
+      __attribute__((always_inline)) {
     const int base = d.base;
     // S^T = K Q^T; A operand: lane holds K[token 16g + n][d = 32ks + 8q4 .. +7]
     f32x4 s[NG];
@@ -399,9 +409,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     for (int g = 0; g < NG; ++g) {
       s[g] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < KSTEP; ++ks)
-        s[g] = E::mfma16(*(const V8*)(kb_ + 16 * g * KROW + ks * 32), qb[ks], s[g]);
+      for (int ks = 0; ks < KSTEP; ++ks) {
+        if constexpr (KD) s[g] = E::mfma16(__builtin_bit_cast(V8, kk[g * KSTEP + ks]), qb[ks], s[g]);
+        else s[g] = E::mfma16(*(const V8*)(kb_ + 16 * g * KROW + ks * 32), qb[ks], s[g]);
+      }
     }
+    after_scores();
     // scores of tokens base + 16g + 4q4 + r for row n; times mult they are in
     // log2 units (plain scores keep the scale folded into the exp argument)
     const bool plain = !(p.softcap > 0.f) && !p.alibi;
@@ -470,7 +483,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
           lx += p0 + p1;
         }
       // V^T operand rows: 32h + 16g' + 4q4 + (n / 4), columns 16db + 4(n % 4)
-      const T* vrow = vbuf + (32 * hh + 4 * q4 + (n >> 2)) * VROW + 4 * (n & 3);
+      const T* vrow = vt + (32 * hh + 4 * q4 + (n >> 2)) * VROW + 4 * (n & 3);
 #pragma unroll
       for (int db = 0; db < DBK; ++db) {
         const i16x4 x0 = lds_read_tr16(vrow + db * 16);
@@ -496,6 +509,134 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     }
   };
 
+  // ---- KD pipeline (D = 128, pages of >= 64 tokens, cache under 4 GiB).  K of
+  // a chunk is loaded straight into the A operands of S^T = K Q^T (16 loads of
+  // 16 tokens x 64 contiguous bytes: the same d order as Q, so the same
+  // products), so only V passes through LDS, in two tiles.  Two register sets
+  // hold K of two chunks, so while chunk c is computed, K of c+1 and c+2 and V
+  // of c+1 are in flight (48 KB per wave against the 32 KB of one chunk).
+  // Step c (s = c % 2):
+  //   a. begin the item of c;  b. request the pages of c+3;  c. load q of c+1;
+  //   d. S^T of c from kreg[s];  e. load K of c+2 into kreg[s];
+  //   f. softmax and P V of c from tile s;
+  //   g. store V of c+1 to tile s^1, loading V of c+2 into the freed registers.
+  // V of c+1 is stored only after c is computed: waiting for it earlier would
+  // also wait for K of c+1 (loads complete in order) and empty the queue.
+  auto kd_pipeline = [&]() __attribute__((always_inline)) {
+    if constexpr (KD) {
+      static_assert(MODE == 1 && OFF32 && NL * RPI == C, "KD: paged cache under 4 GiB");
+      constexpr int NK = NG * KSTEP;
+      const char* kb8 = (const char*)p.k;
+      const char* vb8 = (const char*)p.v;
+      const uint32_t rowb = (uint32_t)(row_elems * sizeof(T));
+      // row of token t of chunk d: t + d0 below bnd, t + d0 + dd from bnd on
+      auto rows_of = [&](const DecodeChunk& d, const int (&e)[NE], int& d0, int& dd, int& bnd)
+          __attribute__((always_inline)) {
+        const int pg0 = div_page(d.base);
+        const int e0 = __builtin_amdgcn_readlane(e[0], 0), e1 = __builtin_amdgcn_readlane(e[0], 1);
+        bnd = (pg0 + 1) * page;
+        d0 = (e0 - pg0) * page;
+        dd = (e1 - e0 - 1) * page;
+      };
+      auto issue_k = [&](const DecodeChunk& d, const int (&e)[NE], u32x4 (&kk)[NK]) __attribute__((always_inline)) {
+        const int hc = (d.ok ? d.hk : 0) / p.kv_split;
+        const uint32_t lane_off = (uint32_t)hc * (uint32_t)(D * sizeof(T)) + (uint32_t)q4 * 16u;
+        int d0, dd, bnd;
+        rows_of(d, e, d0, dd, bnd);
+        const int tl = d.te - 1;
+        const uint32_t off_last = d.ok ? (uint32_t)(tl < bnd ? tl + d0 : tl + d0 + dd) * rowb + lane_off : lane_off;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const int t = d.base + 16 * g + n;
+          uint32_t off = (uint32_t)(t + d0) * rowb + lane_off + (t >= bnd ? (uint32_t)dd * rowb : 0u);
+          if (t > tl || !d.ok) off = d.ok ? off_last : lane_off;
+#pragma unroll
+          for (int ks = 0; ks < KSTEP; ++ks) kk[g * KSTEP + ks] = *(const u32x4*)(kb8 + off + ks * 64);
+        }
+      };
+      // V rows of chunk d; with Swap the registers' chunk is first stored to the
+      // tile vdst piece by piece, each register reloaded right after its store
+      auto issue_v = [&](const DecodeChunk& d, const int (&e)[NE], u32x4 (&vv)[NL], T* vdst, auto Swap)
+          __attribute__((always_inline)) {
+        constexpr bool swap = decltype(Swap)::value;
+        const int hc = (d.ok ? d.hk : 0) / p.kv_split;
+        const uint32_t lane_off = (uint32_t)hc * (uint32_t)(D * sizeof(T)) + (uint32_t)lcol * 16u;
+        int d0, dd, bnd;
+        rows_of(d, e, d0, dd, bnd);
+        const int tl = d.te - 1;
+        const uint32_t off_last = d.ok ? (uint32_t)(tl < bnd ? tl + d0 : tl + d0 + dd) * rowb + lane_off : lane_off;
+        const int t0 = d.base + lane / CHP;
+        const uint32_t off0 = d.ok ? (uint32_t)(t0 + d0) * rowb + lane_off : lane_off;
+        const uint32_t jump = (uint32_t)dd * rowb, stepb = (uint32_t)RPI * rowb;
+        T* const vs = vdst + (lane / CHP) * VROW + lcol * 8;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int t = t0 + RPI * i;
+          uint32_t off = off0 + (uint32_t)i * stepb + (t >= bnd ? jump : 0u);
+          if (t > tl || !d.ok) off = d.ok ? off_last : lane_off;
+          if constexpr (swap) {
+            if (piece_ok) *(u32x4*)(vs + i * RPI * VROW) = vv[i];
+          }
+          vv[i] = *(const u32x4*)(vb8 + off);
+        }
+      };
+      auto issue_q = [&](const DecodeChunk& d, u32x4 (&qs)[KSTEP], float& sls) __attribute__((always_inline)) {
+        const int b = d.ok ? d.b : 0, hk = d.ok ? d.hk : 0;
+        const int hq = hk * p.group + (live ? gq : 0);
+        const uint32_t qoff = (uint32_t)(((b * p.Sq + (live ? sqi : 0)) * p.Hq + hq) * p.head_dim + q4 * 8) *
+                              (uint32_t)sizeof(T);
+        const int qmask = (1 << p.head_shift) - 1;
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks)
+          qs[ks] = *(const u32x4*)((const char*)p.q + ((ks * 32) & qmask) * (int)sizeof(T) + qoff);
+        sls = *(p.alibi ? p.alibi + hq : p.lse_partial);
+      };
+
+      DecodeChunk dc, d1, d2, d3;
+      int ev[2][NE], e0v[NE];
+      u32x4 kreg[2][NK];
+      u32x4 vv[NL];
+      u32x4 qs[KSTEP];
+      float sl = 0.f;
+      next_item(dc);
+      request(dc, e0v);                                 // pages of c0
+      d1 = dc;
+      advance(d1);
+      request(d1, ev[1]);                               // pages of c1
+      issue_q(dc, qs, sl);
+      issue_k(dc, e0v, kreg[0]);
+      issue_v(dc, e0v, vv, vbuf, std::false_type{});
+      d2 = d1;
+      advance(d2);
+      request(d2, ev[0]);                               // pages of c2
+      issue_k(d1, ev[1], kreg[1]);
+      issue_v(d1, ev[1], vv, vbuf, std::true_type{});   // V of c0 to tile 0, load V of c1
+      auto step = [&](auto S) __attribute__((always_inline)) -> bool {
+        constexpr int s0 = decltype(S)::value, s1 = s0 ^ 1;
+        if (dc.first) begin_item(dc, qs, sl);
+        d3 = d2;
+        advance(d3);
+        request(d3, ev[s1]);                            // pages of c+3
+        issue_q(d1, qs, sl);                            // q of c+1
+        compute(dc, kreg[s0], vbuf + s0 * C * VROW, [&] { issue_k(d2, ev[s0], kreg[s0]); });
+        issue_v(d2, ev[s0], vv, vbuf + s1 * C * VROW, std::true_type{});
+        dc = d1;
+        d1 = d2;
+        d2 = d3;
+        return dc.ok;
+      };
+      if (dc.ok) {
+        for (;;) {
+          if (!step(std::integral_constant<int, 0>{})) break;
+          if (!step(std::integral_constant<int, 1>{})) break;
+        }
+      }
+    }
+  };
+  if constexpr (KD) {
+    kd_pipeline();
+    return;
+  }
   // ---- pipeline.  Step j: request the pages of c_{j+2}; store chunk c_j to
   // the LDS tile while loading c_{j+1} into the registers it leaves; compute c_j
   // from LDS while c_{j+1} is in flight.  One chunk in flight per wave reads HBM
@@ -524,7 +665,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
     advance(dq[s0]);                                  // c_{j+2}
     request(dq[s0], ev[s0]);
     issue(dq[s1], ev[s1], kr, vr, qs, sl, std::true_type{});   // store c_j, load c_{j+1}
-    compute(dc);
+    compute(dc, kr, vbuf, [] {});
     dc = dq[s1];
     return dc.ok;
   };
@@ -536,7 +677,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   }
 }
 
-template <class E, int D, int MODE, bool OFF32>
+#ifndef FA_DECODE_KD
+#define FA_DECODE_KD 1
+#endif
+template <class E, int D, int MODE, bool OFF32, bool KD = FA_DECODE_KD && D == 128 && MODE == 1 && OFF32>
 static hipError_t launch_dk(const DecodeParams& p, int cus, hipStream_t s) {
   // resident workgroups per CU (the same on every gfx950 device); computed once,
   // and a concurrent first call at worst computes the same value twice
@@ -544,7 +688,7 @@ static hipError_t launch_dk(const DecodeParams& p, int cus, hipStream_t s) {
   int per_cu = cached.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<E, D, MODE, OFF32>, 64, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel<E, D, MODE, OFF32, KD>, 64, 0) != hipSuccess ||
         nb < 1)
       nb = 1;
     per_cu = nb;
@@ -552,7 +696,7 @@ static hipError_t launch_dk(const DecodeParams& p, int cus, hipStream_t s) {
   }
   const int64_t items = (int64_t)p.B * p.num_splits * p.Hkv;
   const int grid = (int)std::min<int64_t>(items, (int64_t)cus * per_cu);
-  hipLaunchKernelGGL((decode_kernel<E, D, MODE, OFF32>), dim3(grid), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<E, D, MODE, OFF32, KD>), dim3(grid), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
