@@ -274,6 +274,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   // values.  With Swap, the chunk the registers hold is stored to the LDS tile
   // piece by piece, each register reloaded right after its store, so the new
   // chunk's loads leave as soon as the old one starts to arrive.
+  // Rows of chunk d's tokens in the cache (MODE 0 and 1): token t lives in row
+  // t + d0 below bnd and t + d0 + dd from bnd on (MODE 1: the chunk's first page
+  // and, past it, the next one, from the page numbers in lanes 0 and 1 of e).
+  auto page_rows = [&](const DecodeChunk& d, const int (&e)[NE], int& d0, int& dd, int& bnd)
+      __attribute__((always_inline)) {
+    if constexpr (MODE == 0) {
+      d0 = (d.ok ? d.b : 0) * page; dd = 0; bnd = 0x7fffffff;
+    } else if constexpr (MODE == 1) {
+      const int pg0 = div_page(d.base);
+      const int e0 = __builtin_amdgcn_readlane(e[0], 0), e1 = __builtin_amdgcn_readlane(e[0], 1);
+      bnd = (pg0 + 1) * page; d0 = (e0 - pg0) * page; dd = (e1 - e0 - 1) * page;
+    } else {
+      d0 = 0; dd = 0; bnd = 0x7fffffff;
+    }
+  };
+  // The item's query rows (rows past the group read row 0) and ALiBi slopes (a
+  // stand-in address without slopes), as raw loaded values.
+  auto issue_q = [&](const DecodeChunk& d, u32x4 (&qs)[KSTEP], float& sls) __attribute__((always_inline)) {
+    const int b = d.ok ? d.b : 0, hk = d.ok ? d.hk : 0;
+    const int hq = hk * p.group + (live ? gq : 0);
+    // q holds at most 2^31 bytes (checked on the host): a 32-bit byte offset per
+    // lane from a wave-uniform base, the piece's place within its head uniform per ks
+    const uint32_t qoff = (uint32_t)(((b * p.Sq + (live ? sqi : 0)) * p.Hq + hq) * p.head_dim + q4 * 8) *
+                          (uint32_t)sizeof(T);
+    const int qmask = (1 << p.head_shift) - 1;   // element within its head (all ones: one head)
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks)
+      qs[ks] = *(const u32x4*)((const char*)p.q + ((ks * 32) & qmask) * (int)sizeof(T) + qoff);
+    sls = *(p.alibi ? p.alibi + hq : p.lse_partial);
+  };
   auto issue = [&](const DecodeChunk& d, const int (&e)[NE], u32x4 (&kr)[NL], u32x4 (&vr)[NL],
                    u32x4 (&qs)[KSTEP], float& sls, auto Swap) __attribute__((always_inline)) {
     constexpr bool swap = decltype(Swap)::value;
@@ -311,11 +341,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
         }
       } else {
         int d0, dd, bnd;                      // row(t) = t + d0 below bnd, t + d0 + dd from bnd on
-        if constexpr (MODE == 0) {
-          d0 = b * page; dd = 0; bnd = 0x7fffffff;
-        } else {
-          bnd = (pg0 + 1) * page; d0 = (e0 - pg0) * page; dd = (e1 - e0 - 1) * page;
-        }
+        page_rows(d, e, d0, dd, bnd);
         const int tlast = (tl < bnd ? tl + d0 : tl + d0 + dd);
         const uint32_t off_last = d.ok ? (uint32_t)tlast * rowb + lane_off : lane_off;
         const int t0 = d.base + lr;
@@ -351,16 +377,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
         vr[i] = *(const u32x4*)(vh + row * row_elems + c * 8);
       }
     }
-    const int hq = hk * p.group + (live ? gq : 0);
-    // q holds at most 2^31 bytes (checked on the host): a 32-bit byte offset per
-    // lane from a wave-uniform base, the piece's place within its head uniform per ks
-    const uint32_t qoff = (uint32_t)(((b * p.Sq + (live ? sqi : 0)) * p.Hq + hq) * p.head_dim + q4 * 8) *
-                          (uint32_t)sizeof(T);
-    const int qmask = (1 << p.head_shift) - 1;   // element within its head (all ones: one head)
-#pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks)
-      qs[ks] = *(const u32x4*)((const char*)p.q + ((ks * 32) & qmask) * (int)sizeof(T) + qoff);
-    sls = *(p.alibi ? p.alibi + hq : p.lse_partial);
+    issue_q(d, qs, sls);
   };
   // ---- per-item row state.  Row n sees tokens [rlo, rhi] of the item; every
   // live row sees [wlo, whi], so chunks inside it need no masking.
@@ -529,20 +546,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
       const char* kb8 = (const char*)p.k;
       const char* vb8 = (const char*)p.v;
       const uint32_t rowb = (uint32_t)(row_elems * sizeof(T));
-      // row of token t of chunk d: t + d0 below bnd, t + d0 + dd from bnd on
-      auto rows_of = [&](const DecodeChunk& d, const int (&e)[NE], int& d0, int& dd, int& bnd)
-          __attribute__((always_inline)) {
-        const int pg0 = div_page(d.base);
-        const int e0 = __builtin_amdgcn_readlane(e[0], 0), e1 = __builtin_amdgcn_readlane(e[0], 1);
-        bnd = (pg0 + 1) * page;
-        d0 = (e0 - pg0) * page;
-        dd = (e1 - e0 - 1) * page;
-      };
       auto issue_k = [&](const DecodeChunk& d, const int (&e)[NE], u32x4 (&kk)[NK]) __attribute__((always_inline)) {
         const int hc = (d.ok ? d.hk : 0) / p.kv_split;
         const uint32_t lane_off = (uint32_t)hc * (uint32_t)(D * sizeof(T)) + (uint32_t)q4 * 16u;
         int d0, dd, bnd;
-        rows_of(d, e, d0, dd, bnd);
+        page_rows(d, e, d0, dd, bnd);
         const int tl = d.te - 1;
         const uint32_t off_last = d.ok ? (uint32_t)(tl < bnd ? tl + d0 : tl + d0 + dd) * rowb + lane_off : lane_off;
 #pragma unroll
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
         const int hc = (d.ok ? d.hk : 0) / p.kv_split;
         const uint32_t lane_off = (uint32_t)hc * (uint32_t)(D * sizeof(T)) + (uint32_t)lcol * 16u;
         int d0, dd, bnd;
-        rows_of(d, e, d0, dd, bnd);
+        page_rows(d, e, d0, dd, bnd);
         const int tl = d.te - 1;
         const uint32_t off_last = d.ok ? (uint32_t)(tl < bnd ? tl + d0 : tl + d0 + dd) * rowb + lane_off : lane_off;
         const int t0 = d.base + lane / CHP;
@@ -580,18 +588,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
           vv[i] = *(const u32x4*)(vb8 + off);
         }
       };
-      auto issue_q = [&](const DecodeChunk& d, u32x4 (&qs)[KSTEP], float& sls) __attribute__((always_inline)) {
-        const int b = d.ok ? d.b : 0, hk = d.ok ? d.hk : 0;
-        const int hq = hk * p.group + (live ? gq : 0);
-        const uint32_t qoff = (uint32_t)(((b * p.Sq + (live ? sqi : 0)) * p.Hq + hq) * p.head_dim + q4 * 8) *
-                              (uint32_t)sizeof(T);
-        const int qmask = (1 << p.head_shift) - 1;
-#pragma unroll
-        for (int ks = 0; ks < KSTEP; ++ks)
-          qs[ks] = *(const u32x4*)((const char*)p.q + ((ks * 32) & qmask) * (int)sizeof(T) + qoff);
-        sls = *(p.alibi ? p.alibi + hq : p.lse_partial);
-      };
-
       DecodeChunk dc, d1, d2, d3;
       int ev[2][NE], e0v[NE];
       u32x4 kreg[2][NK];
