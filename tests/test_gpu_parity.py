@@ -147,6 +147,10 @@ def test_c5_decode_with_one_token_append(c5):
 
 
 def test_c5_paged_equals_dense_cache_bitexact(c5):
+    """The paged gather equals the dense cache bit for bit.  At D = 128 the paged
+    call runs the decode form that loads K straight into MFMA operand registers
+    and the dense call the form that stages K in LDS, so this also checks that
+    the two forms compute the same products in the same order."""
     kd = inputs.dense_cache_from_pool(c5["k_pool"], c5["block_table"], c5["cache_seqlens"])
     vd = inputs.dense_cache_from_pool(c5["v_pool"], c5["block_table"], c5["cache_seqlens"])
     a = run_paged(c5)
