@@ -673,6 +673,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_DECODE_WP
   }
 }
 
+// 1: D = 128 on a paged cache under 4 GiB runs the KD form (K in operand
+// registers, V in two LDS tiles); 0: the LDS form everywhere
 #ifndef FA_DECODE_KD
 #define FA_DECODE_KD 1
 #endif
