@@ -72,6 +72,22 @@ struct BF16 {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Scheduling of a block that forms N values of P: each exponential (a TRANS
+// instruction) is placed after G other VALU instructions, so the wave's
+// exponentials are spread among its FMAs, packs and adds instead of issuing in
+// runs; the transcendental unit then works beside the VALU.  Changes only the
+// order of independent instructions.
+template <int N, int G>
+__device__ __forceinline__ void spread_exponentials() {
+  if constexpr (G > 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x002, G, 0);   // VALU (not TRANS, not MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);   // TRANS
+    }
+  }
+}
+
 // s_waitcnt vmcnt(0): every vector-memory access issued so far has completed.
 // Placed before a loop, it tells the compiler that registers loaded before the
 // loop are ready, so waits inside the loop count only the loop's own loads.

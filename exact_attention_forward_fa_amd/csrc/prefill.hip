@@ -53,6 +53,9 @@ template <class E> constexpr float precise_out_pp() { return std::is_same_v<E, B
 #endif
 // 1: the ping-pong kernel's lean softmax phase (lazy max, fp32 sum only) for
 // plain masks; softcap and ALiBi keep the full phase (see prefill_pp_kernel)
+#ifndef FA_PREFILL_TRANS_GROUPS
+#define FA_PREFILL_TRANS_GROUPS 3    // VALU instructions placed before each exponential of P
+#endif
 #ifndef FA_PP_LEAN
 #define FA_PP_LEAN 1
 #endif
@@ -61,6 +64,7 @@ template <class E> constexpr float precise_out_pp() { return std::is_same_v<E, B
 #endif
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+
 
 // LDS row strides (elements) of the K and V tiles.  Padding instead of an XOR
 // swizzle keeps every LDS read at "one base register + immediate offset":
@@ -367,6 +371,9 @@ void prefill_kernel(PrefillParams p) {
         }
       lxs[rb] = ax;
     }
+    // 8-wave workgroups only: the 4-wave (window, D = 96) instances measured
+    // 1-3% slower with the exponentials spread
+    spread_exponentials<RB * KB * 16, NW == 8 ? FA_PREFILL_TRANS_GROUPS : 0>();
   };
 
   // One tile for the wave's RB row blocks; mask arithmetic runs only when edge is set.
